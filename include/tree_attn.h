@@ -1,0 +1,191 @@
+/*
+ * tree_attn.h - C ABI of the Medusa tree-verify step on MI355X (gfx950).
+ *
+ * One verify step of Medusa speculative decoding, for a batch of sequences
+ * that each submit a tree of up to 64 candidate tokens:
+ *
+ *   tree_attn_verify    every tree node attends to the sequence's paged KV
+ *                       cache plus its own ancestors (and itself) in the tree,
+ *                       with RoPE applied at position ctx_len + depth;
+ *   tree_accept_greedy  greedy acceptance of the longest root-to-node path
+ *                       whose candidate tokens equal the base model's greedy
+ *                       predictions;
+ *   kv_commit_path      writes the accepted path's K/V rows into the pages.
+ *
+ * Sources: vLLM issue #1171 "[Discussion] Will vLLM consider using
+ * Speculative Sampling to accelerating LLM decoding?" (decode with several new
+ * tokens over an existing paged KV cache; a tree mask inside the cached-KV
+ * attention; block-table update on acceptance), TensorRT-LLM issue #1946
+ * "How to use Medusa to support non llama models?" (position offsets fed to
+ * RoPE for the Medusa tokens), LMDeploy PR #1231 "[WIP] support Medusa"
+ * (evaluate_posterior at LM-head temperature 0; TreeMask on Flash Decoding),
+ * mlc-llm issue #2319 "[Feature Request] Medusa support" (tree attention and
+ * the KV-cache update as the two hard parts).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *    contiguous.  The library allocates nothing, keeps no global state, never
+ *    synchronises the device with the host, and enqueues all work on
+ *    desc->stream (a hipStream_t; NULL = the default stream).
+ *  - Element type of q, k_new, v_new, kv_pages and out is desc->dtype
+ *    (TA_BF16 or TA_F32); index tensors are int32.
+ *  - Layouts (B = batch, T = t_max, H = num_heads, Hkv = num_kv_heads,
+ *    d = head_dim, P = block_size = 16):
+ *        q, out            [B][T][H][d]
+ *        k_new, v_new      [B][T][Hkv][d]      (k_new not yet rotated)
+ *        kv_pages          [num_blocks][2][Hkv][P][d]   (index 0 = K, 1 = V;
+ *                                               cached K is stored rotated)
+ *        block_table       [B][max_blocks_per_seq]      physical block ids
+ *        ctx_lens          [B]     committed tokens per sequence
+ *        tree_parent       [B][T]  -1 for the root (node 0); parent[i] < i
+ *                                  for real nodes; -2 for padding nodes,
+ *                                  which must form a suffix
+ *        tree_depth        [B][T]  depth of each node (root 0)
+ *        node_argmax       [B][T]  base model's greedy token after node i
+ *        cand_tokens       [B][T]  candidate token carried by node i
+ *        accept_len        [B]     accepted nodes including the root
+ *        accept_path       [B][T]  accepted node ids by depth, -1 beyond
+ *        rope_cos_sin      [rope_max_pos][d/2][2] fp32 (cos, sin) of
+ *                                  pos * base^(-2k/d), see tree_attn_rope_table
+ *  - Token t of sequence b lives in page block_table[b][t / 16], slot t % 16.
+ *  - RoPE is rotate-half: pairs (x_k, x_{k+d/2}), y_k = x_k*c - x_{k+d/2}*s,
+ *    y_{k+d/2} = x_{k+d/2}*c + x_k*s, at position ctx_len[b] + depth.
+ *  - Return value: TA_OK (0) or a negative TA_ERR_* code.  Every check that
+ *    can be made on the host is made before anything is enqueued; nothing
+ *    aborts and no exception crosses the ABI.  Device-resident values
+ *    (ctx_lens, block ids, tree structure, accepted paths) are bounds-checked
+ *    inside the kernels: an out-of-range value never causes an out-of-bounds
+ *    access, but the affected outputs are unspecified (ctx_len is clamped to
+ *    [0, max_ctx_len]; an out-of-range page is skipped).
+ *  - Calls are asynchronous; a launch failure is reported as TA_ERR_LAUNCH.
+ *    Two calls that share a workspace must not run concurrently.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ta_dtype { TA_BF16 = 0, TA_F32 = 1 };
+
+/* desc->flags bits */
+enum ta_flags {
+  TA_FLAG_SIMPLE_KERNEL = 1   /* verify with the plain one-wavefront-per-node  */
+                              /* kernel even where the MFMA kernel applies     */
+};
+
+enum ta_status {
+  TA_OK = 0,
+  TA_ERR_NULL_POINTER = -1,   /* a required pointer is NULL                  */
+  TA_ERR_BAD_DIMS = -2,       /* batch/t_max/heads/blocks not positive, etc. */
+  TA_ERR_DTYPE = -3,          /* dtype not TA_BF16 / TA_F32                  */
+  TA_ERR_TREE_TOO_LARGE = -4, /* t_max > 64                                  */
+  TA_ERR_HEAD_DIM = -5,       /* head_dim not 64 or 128                      */
+  TA_ERR_HEADS = -6,          /* num_heads not a multiple of num_kv_heads    */
+  TA_ERR_BLOCK_SIZE = -7,     /* block_size != 16                            */
+  TA_ERR_WORKSPACE = -8,      /* workspace NULL or smaller than required     */
+  TA_ERR_ROPE_TABLE = -9,     /* rope table missing or rope_max_pos too small*/
+  TA_ERR_CAPACITY = -10,      /* max_blocks_per_seq*16 < max_ctx_len         */
+  TA_ERR_LAUNCH = -11         /* the HIP runtime rejected a launch           */
+};
+
+typedef struct tree_attn_desc {
+  int32_t batch;              /* B                                            */
+  int32_t t_max;              /* T, nodes per tree incl. padding, 1..64       */
+  int32_t num_heads;          /* H query heads                                */
+  int32_t num_kv_heads;       /* Hkv KV heads, H % Hkv == 0                   */
+  int32_t head_dim;           /* d, 64 or 128                                 */
+  int32_t block_size;         /* tokens per page, must be 16                  */
+  int32_t max_blocks_per_seq; /* columns of block_table                       */
+  int32_t num_blocks;         /* pages in kv_pages                            */
+  int32_t max_ctx_len;        /* host-known upper bound on every ctx_lens[b]; */
+                              /* sizes the launch grid, never read back       */
+  int32_t dtype;              /* enum ta_dtype                                */
+  float scale;                /* softmax scale; <= 0 selects 1/sqrt(d)        */
+  const float* rope_cos_sin;  /* device fp32 table, see layout above          */
+  int32_t rope_max_pos;       /* rows of rope_cos_sin, >= max_ctx_len + t_max */
+  void* workspace;            /* device scratch owned by the caller           */
+  size_t workspace_bytes;     /* its size, >= tree_attn_workspace_size(desc)  */
+  void* stream;               /* hipStream_t                                  */
+  int32_t flags;              /* enum ta_flags, 0 by default                  */
+} tree_attn_desc;
+
+/* Tree attention (vLLM #1171: several new tokens over a paged KV cache under
+ * a tree mask; TensorRT-LLM #1946: RoPE position offsets; LMDeploy #1231:
+ * TreeMask over split-KV Flash Decoding).
+ * For every real node i of sequence b and query head h (kv head
+ * h / (H/Hkv)):
+ *   keys   = cached K of tokens 0..ctx_len[b]-1 (as stored), then the tree
+ *            keys RoPE(k_new[b][j], ctx_len[b] + depth[j]) for the nodes j
+ *            that are ancestors of i or i itself;
+ *   values = cached V, then v_new[b][j] for the same j;
+ *   out[b][i][h] = softmax(scale * RoPE(q[b][i][h], ctx_len[b] + depth[i])
+ *                  . keys) . values, accumulated in fp32 and rounded to
+ *                  dtype (round to nearest even).
+ * Padding rows of out are written as zeros.  kv_pages is only read.
+ * Needs desc->workspace of tree_attn_workspace_size(desc) bytes that was
+ * zero-filled once (tree_attn_workspace_init); every call leaves it zeroed
+ * again.  Errors: every TA_ERR_* code. */
+int tree_attn_verify(const tree_attn_desc* desc, const void* q, const void* k_new,
+                     const void* v_new, const void* kv_pages,
+                     const int32_t* block_table, const int32_t* ctx_lens,
+                     const int32_t* tree_parent, const int32_t* tree_depth,
+                     void* out);
+
+/* Greedy acceptance (LMDeploy #1231 evaluate_posterior at temperature 0).
+ * Node c (c >= 1) matches iff cand_tokens[b][c] == node_argmax[b][parent(c)];
+ * a node is accepted iff every edge on its root path matches.  The end node
+ * is the deepest accepted node, the smallest index among equals;
+ * accept_len[b] = depth(end) + 1 and accept_path[b][k] = the accepted node at
+ * depth k for k < accept_len[b], -1 after.  The root's own candidate token is
+ * never checked.  The bonus token of the step is
+ * node_argmax[b][accept_path[b][accept_len[b]-1]].
+ * Uses batch, t_max and stream of desc; other fields are not read.  Output
+ * is bit-exact: integer work only. */
+int tree_accept_greedy(const tree_attn_desc* desc, const int32_t* node_argmax,
+                       const int32_t* cand_tokens, const int32_t* tree_parent,
+                       int32_t* accept_len, int32_t* accept_path);
+
+/* KV commit (mlc-llm #2319 KV-cache update; vLLM #1171 block-table update).
+ * For i < accept_len[b], node n = accept_path[b][i], position
+ * p = ctx_len[b] + i: page block_table[b][p/16], slot p%16 receives
+ *   K = RoPE(k_new[b][n], p) computed in fp32 from rope_cos_sin[p] as
+ *       (x1*c) - (x2*s) and (x2*c) + (x1*s), each operation rounded, no fused
+ *       multiply-add, then rounded to dtype (nearest even);
+ *   V = v_new[b][n], bit for bit.
+ * No other byte of kv_pages changes; ctx_lens is not modified (the caller
+ * adds accept_len).  The caller reserves pages so that ctx_len + accept_len
+ * fits in max_blocks_per_seq*16 and frees unused pages itself. */
+int kv_commit_path(const tree_attn_desc* desc, const void* k_new, const void* v_new,
+                   const int32_t* accept_len, const int32_t* accept_path,
+                   void* kv_pages, const int32_t* block_table,
+                   const int32_t* ctx_lens);
+
+/* Bytes of workspace tree_attn_verify needs for this descriptor (0 if the
+ * descriptor is invalid).  Pure host computation. */
+size_t tree_attn_workspace_size(const tree_attn_desc* desc);
+
+/* Zero-fills desc->workspace (desc->workspace_bytes bytes) on desc->stream
+ * with a fill kernel.  Call once after allocating a workspace. */
+int tree_attn_workspace_init(const tree_attn_desc* desc);
+
+/* Fills table[pos][k][0..1] = (cos, sin)(pos * base^(-2k/head_dim)) for
+ * pos < max_pos, k < head_dim/2: the angle is formed in fp64 and each value
+ * rounded once to fp32 (TensorRT-LLM #1946 position offsets; neox-style
+ * RoPE).  table is a device buffer of max_pos*head_dim floats. */
+int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* table,
+                         void* stream);
+
+/* Static description of a status code. */
+const char* tree_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,229 @@
+"""ctypes binding of libtree_attn.so (see include/tree_attn.h).
+
+Argument marshalling only: every step of the verify / accept / commit path
+runs in the HIP kernels of the library.  Tensors are PyTorch device tensors
+(PyTorch provides device memory and streams); their data pointers and torch's
+current stream are handed to the C ABI.  Before a call, the shapes, dtypes,
+devices and contiguity of the tensors are checked against the descriptor, so a
+kernel never sees an operand smaller than its grid assumes.
+
+The library must be built (python -m medusa_tree_attention_attn_amd.build);
+there is no fallback of any kind if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch  # first: the library then binds to the HIP runtime torch loaded
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtree_attn.so")
+
+TA_BF16 = 0
+TA_F32 = 1
+TA_FLAG_SIMPLE_KERNEL = 1
+
+STATUS = {
+    0: "TA_OK", -1: "TA_ERR_NULL_POINTER", -2: "TA_ERR_BAD_DIMS", -3: "TA_ERR_DTYPE",
+    -4: "TA_ERR_TREE_TOO_LARGE", -5: "TA_ERR_HEAD_DIM", -6: "TA_ERR_HEADS",
+    -7: "TA_ERR_BLOCK_SIZE", -8: "TA_ERR_WORKSPACE", -9: "TA_ERR_ROPE_TABLE",
+    -10: "TA_ERR_CAPACITY", -11: "TA_ERR_LAUNCH",
+}
+EXPORTED = (
+    "tree_attn_verify", "tree_accept_greedy", "kv_commit_path",
+    "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_rope_table",
+    "tree_attn_strerror",
+)
+
+
+class TreeAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("t_max", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("rope_cos_sin", ctypes.c_void_p),
+        ("rope_max_pos", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
+    ]
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({strerror(code)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the shared library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m medusa_tree_attention_attn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(TreeAttnDesc)
+    sig = {
+        "tree_attn_verify": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
+        "tree_accept_greedy": (ctypes.c_int, [D, P, P, P, P, P]),
+        "kv_commit_path": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
+        "tree_attn_workspace_size": (ctypes.c_size_t, [D]),
+        "tree_attn_workspace_init": (ctypes.c_int, [D]),
+        "tree_attn_rope_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_float,
+                                                ctypes.c_int32, P, P]),
+        "tree_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().tree_attn_strerror(int(code)).decode()
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise TreeAttnError(code, what)
+
+
+def current_stream_handle(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# ------------------------------------------------------------ descriptor --
+
+def make_desc(*, batch, t_max, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+              num_blocks, max_ctx_len, dtype, rope_table=None, rope_max_pos=0,
+              workspace=None, workspace_bytes=0, scale=0.0, stream=None, flags=0,
+              block_size=16) -> TreeAttnDesc:
+    d = TreeAttnDesc()
+    d.batch, d.t_max = batch, t_max
+    d.num_heads, d.num_kv_heads, d.head_dim = num_heads, num_kv_heads, head_dim
+    d.block_size = block_size
+    d.max_blocks_per_seq, d.num_blocks, d.max_ctx_len = max_blocks_per_seq, num_blocks, max_ctx_len
+    d.dtype = dtype
+    d.scale = scale
+    d.rope_cos_sin = _ptr(rope_table)
+    d.rope_max_pos = rope_max_pos
+    d.workspace = _ptr(workspace)
+    d.workspace_bytes = workspace_bytes
+    d.stream = stream
+    d.flags = flags
+    return d
+
+
+def _dtype_of(desc):
+    return torch.bfloat16 if desc.dtype == TA_BF16 else torch.float32
+
+
+def _expect(t, shape, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, descriptor expects {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# ---------------------------------------------------------------- calls --
+
+def tree_attn_verify(desc, q, k_new, v_new, kv_pages, block_table, ctx_lens, tree_parent,
+                     tree_depth, out):
+    B, T, H, Hkv, d = desc.batch, desc.t_max, desc.num_heads, desc.num_kv_heads, desc.head_dim
+    dt = _dtype_of(desc)
+    _expect(q, (B, T, H, d), dt, "q")
+    _expect(k_new, (B, T, Hkv, d), dt, "k_new")
+    _expect(v_new, (B, T, Hkv, d), dt, "v_new")
+    _expect(kv_pages, (desc.num_blocks, 2, Hkv, 16, d), dt, "kv_pages")
+    _expect(block_table, (B, desc.max_blocks_per_seq), torch.int32, "block_table")
+    _expect(ctx_lens, (B,), torch.int32, "ctx_lens")
+    _expect(tree_parent, (B, T), torch.int32, "tree_parent")
+    _expect(tree_depth, (B, T), torch.int32, "tree_depth")
+    _expect(out, (B, T, H, d), dt, "out")
+    rc = load().tree_attn_verify(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                 _ptr(kv_pages), _ptr(block_table), _ptr(ctx_lens),
+                                 _ptr(tree_parent), _ptr(tree_depth), _ptr(out))
+    _check(rc, "tree_attn_verify")
+
+
+def tree_accept_greedy(desc, node_argmax, cand_tokens, tree_parent, accept_len, accept_path):
+    B, T = desc.batch, desc.t_max
+    for t, shp, name in ((node_argmax, (B, T), "node_argmax"), (cand_tokens, (B, T), "cand_tokens"),
+                         (tree_parent, (B, T), "tree_parent"), (accept_len, (B,), "accept_len"),
+                         (accept_path, (B, T), "accept_path")):
+        _expect(t, shp, torch.int32, name)
+    rc = load().tree_accept_greedy(ctypes.byref(desc), _ptr(node_argmax), _ptr(cand_tokens),
+                                   _ptr(tree_parent), _ptr(accept_len), _ptr(accept_path))
+    _check(rc, "tree_accept_greedy")
+
+
+def kv_commit_path(desc, k_new, v_new, accept_len, accept_path, kv_pages, block_table, ctx_lens):
+    B, T, Hkv, d = desc.batch, desc.t_max, desc.num_kv_heads, desc.head_dim
+    dt = _dtype_of(desc)
+    _expect(k_new, (B, T, Hkv, d), dt, "k_new")
+    _expect(v_new, (B, T, Hkv, d), dt, "v_new")
+    _expect(accept_len, (B,), torch.int32, "accept_len")
+    _expect(accept_path, (B, T), torch.int32, "accept_path")
+    _expect(kv_pages, (desc.num_blocks, 2, Hkv, 16, d), dt, "kv_pages")
+    _expect(block_table, (B, desc.max_blocks_per_seq), torch.int32, "block_table")
+    _expect(ctx_lens, (B,), torch.int32, "ctx_lens")
+    rc = load().kv_commit_path(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(accept_len),
+                               _ptr(accept_path), _ptr(kv_pages), _ptr(block_table),
+                               _ptr(ctx_lens))
+    _check(rc, "kv_commit_path")
+
+
+def tree_attn_workspace_size(desc) -> int:
+    return int(load().tree_attn_workspace_size(ctypes.byref(desc)))
+
+
+def tree_attn_workspace_init(desc):
+    _check(load().tree_attn_workspace_init(ctypes.byref(desc)), "tree_attn_workspace_init")
+
+
+def tree_attn_rope_table(head_dim, base, max_pos, table, stream=None):
+    if isinstance(table, torch.Tensor):
+        _expect(table, (max_pos, head_dim // 2, 2), torch.float32, "rope table")
+    rc = load().tree_attn_rope_table(int(head_dim), float(base), int(max_pos), _ptr(table), stream)
+    _check(rc, "tree_attn_rope_table")
+
+
+def tree_attn_strerror(code: int) -> str:
+    return strerror(code)
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

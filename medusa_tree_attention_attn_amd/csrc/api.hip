@@ -1,0 +1,164 @@
+// C ABI of the tree-verify library: host-side validation, split planning and
+// dispatch.  No allocation, no device->host synchronisation, no global state.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "plan.h"
+
+using namespace ta;
+
+namespace {
+
+int check_common(const tree_attn_desc* d) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->t_max <= 0 || d->num_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->max_blocks_per_seq <= 0 || d->num_blocks <= 0 || d->max_ctx_len < 0)
+    return TA_ERR_BAD_DIMS;
+  if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  if (d->dtype != TA_BF16 && d->dtype != TA_F32) return TA_ERR_DTYPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return TA_ERR_HEAD_DIM;
+  if (d->num_heads % d->num_kv_heads != 0) return TA_ERR_HEADS;
+  if (d->block_size != kPage) return TA_ERR_BLOCK_SIZE;
+  if (d->batch > 65535) return TA_ERR_BAD_DIMS;
+  if ((int64_t)d->max_blocks_per_seq * kPage < (int64_t)d->max_ctx_len) return TA_ERR_CAPACITY;
+  if (!d->rope_cos_sin || (int64_t)d->rope_max_pos < (int64_t)d->max_ctx_len + d->t_max)
+    return TA_ERR_ROPE_TABLE;
+  return TA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t tree_attn_workspace_size(const tree_attn_desc* d) {
+  if (check_common(d) != TA_OK) return 0;
+  return make_plan(*d).bytes;
+}
+
+int tree_attn_workspace_init(const tree_attn_desc* d) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->workspace_bytes == 0) return TA_OK;
+  if (!d->workspace) return TA_ERR_NULL_POINTER;
+  return status_of(launch_fill_zero(d->workspace, d->workspace_bytes,
+                                    static_cast<hipStream_t>(d->stream)));
+}
+
+int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
+                     const void* v_new, const void* kv_pages, const int32_t* block_table,
+                     const int32_t* ctx_lens, const int32_t* tree_parent,
+                     const int32_t* tree_depth, void* out) {
+  const int rc = check_common(d);
+  if (rc != TA_OK) return rc;
+  if (!q || !k_new || !v_new || !kv_pages || !block_table || !ctx_lens || !tree_parent ||
+      !tree_depth || !out)
+    return TA_ERR_NULL_POINTER;
+  const Plan plan = make_plan(*d);
+  if (plan.bytes > 0 && (!d->workspace || d->workspace_bytes < plan.bytes))
+    return TA_ERR_WORKSPACE;
+
+  VerifyParams p{};
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.kv_pages = kv_pages;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.tree_parent = tree_parent;
+  p.tree_depth = tree_depth;
+  p.out = out;
+  p.rope = d->rope_cos_sin;
+  p.B = d->batch;
+  p.T = d->t_max;
+  p.H = d->num_heads;
+  p.Hkv = d->num_kv_heads;
+  p.D = d->head_dim;
+  p.max_blocks = d->max_blocks_per_seq;
+  p.num_blocks = d->num_blocks;
+  p.max_ctx = d->max_ctx_len;
+  p.rope_max_pos = d->rope_max_pos;
+  p.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
+  p.chunk = plan.chunk;
+  p.splits = plan.splits;
+  hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  if (plan.mfma) {
+    char* ws = static_cast<char*>(d->workspace);
+    p.ws_count = reinterpret_cast<int32_t*>(ws + plan.off_count);
+    p.ws_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
+    p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
+    return status_of(launch_verify_mfma(p, stream));
+  }
+  return status_of(launch_verify_simple(p, d->dtype, stream));
+}
+
+int tree_accept_greedy(const tree_attn_desc* d, const int32_t* node_argmax,
+                       const int32_t* cand_tokens, const int32_t* tree_parent,
+                       int32_t* accept_len, int32_t* accept_path) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->t_max <= 0 || d->batch > (1 << 30)) return TA_ERR_BAD_DIMS;
+  if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  if (!node_argmax || !cand_tokens || !tree_parent || !accept_len || !accept_path)
+    return TA_ERR_NULL_POINTER;
+  return status_of(launch_accept(node_argmax, cand_tokens, tree_parent, accept_len,
+                                 accept_path, d->batch, d->t_max,
+                                 static_cast<hipStream_t>(d->stream)));
+}
+
+int kv_commit_path(const tree_attn_desc* d, const void* k_new, const void* v_new,
+                   const int32_t* accept_len, const int32_t* accept_path, void* kv_pages,
+                   const int32_t* block_table, const int32_t* ctx_lens) {
+  const int rc = check_common(d);
+  if (rc != TA_OK) return rc;
+  if (!k_new || !v_new || !accept_len || !accept_path || !kv_pages || !block_table ||
+      !ctx_lens)
+    return TA_ERR_NULL_POINTER;
+  CommitParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.accept_len = accept_len;
+  p.accept_path = accept_path;
+  p.kv_pages = kv_pages;
+  p.block_table = block_table;
+  p.ctx_lens = ctx_lens;
+  p.rope = d->rope_cos_sin;
+  p.B = d->batch;
+  p.T = d->t_max;
+  p.Hkv = d->num_kv_heads;
+  p.D = d->head_dim;
+  p.max_blocks = d->max_blocks_per_seq;
+  p.num_blocks = d->num_blocks;
+  p.max_ctx = d->max_ctx_len;
+  p.rope_max_pos = d->rope_max_pos;
+  return status_of(launch_commit(p, d->dtype, static_cast<hipStream_t>(d->stream)));
+}
+
+int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* table,
+                         void* stream) {
+  if (!table) return TA_ERR_NULL_POINTER;
+  if (head_dim != 64 && head_dim != 128) return TA_ERR_HEAD_DIM;
+  if (max_pos <= 0 || !(base > 1.0f)) return TA_ERR_BAD_DIMS;
+  return status_of(launch_rope_table(head_dim, base, max_pos, table,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+const char* tree_attn_strerror(int status) {
+  switch (status) {
+    case TA_OK: return "ok";
+    case TA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case TA_ERR_BAD_DIMS: return "invalid dimensions in the descriptor";
+    case TA_ERR_DTYPE: return "unsupported dtype (TA_BF16 or TA_F32)";
+    case TA_ERR_TREE_TOO_LARGE: return "t_max exceeds 64 nodes";
+    case TA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case TA_ERR_HEADS: return "num_heads must be a multiple of num_kv_heads";
+    case TA_ERR_BLOCK_SIZE: return "block_size must be 16";
+    case TA_ERR_WORKSPACE: return "workspace missing or smaller than tree_attn_workspace_size";
+    case TA_ERR_ROPE_TABLE: return "rope table missing or rope_max_pos < max_ctx_len + t_max";
+    case TA_ERR_CAPACITY: return "max_blocks_per_seq * 16 < max_ctx_len";
+    case TA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Host-side launchers of the kernels behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace ta {
+
+// One wavefront per (node, head, sequence), any head_dim in {64, 128},
+// bf16 or fp32.  Plain and slow; no workspace.
+hipError_t launch_verify_simple(const VerifyParams& p, int dtype, hipStream_t stream);
+
+// MFMA split-KV kernel for bf16, head_dim 128, with the split combine fused
+// into the last-arriving work item of each (sequence, head).
+hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream);
+
+hipError_t launch_accept(const int32_t* node_argmax, const int32_t* cand_tokens,
+                         const int32_t* tree_parent, int32_t* accept_len,
+                         int32_t* accept_path, int B, int T, hipStream_t stream);
+
+struct CommitParams {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* accept_len;
+  const int32_t* accept_path;
+  void* kv_pages;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const float* rope;
+  int B, T, Hkv, D, max_blocks, num_blocks, max_ctx, rope_max_pos;
+};
+hipError_t launch_commit(const CommitParams& p, int dtype, hipStream_t stream);
+
+hipError_t launch_rope_table(int head_dim, float base, int max_pos, float* table,
+                             hipStream_t stream);
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace ta

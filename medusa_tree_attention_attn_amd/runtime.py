@@ -1,0 +1,74 @@
+"""Host-side driver of one Medusa tree-verify step on one GPU.
+
+`TreeVerifier` owns what a step needs besides the caller's tensors: the
+descriptor, the RoPE (cos, sin) table (filled by the library's own kernel)
+and the split-KV workspace (allocated once through PyTorch and zero-filled by
+the library).  Each call runs on torch's current stream; nothing here
+synchronises with the device or computes anything itself.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_greedy,
+                   tree_attn_rope_table, tree_attn_verify, tree_attn_workspace_init,
+                   tree_attn_workspace_size)
+
+ROPE_BASE = 10000.0
+
+
+class TreeVerifier:
+    def __init__(self, *, batch: int, t_max: int, num_heads: int, num_kv_heads: int,
+                 head_dim: int, max_blocks_per_seq: int, num_blocks: int, max_ctx_len: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", rope_base: float = ROPE_BASE,
+                 scale: float = 0.0, flags: int = 0, rope_max_pos: Optional[int] = None):
+        _lib.load()
+        self.device = torch.device(device)
+        self.dtype = dtype
+        self.rope_max_pos = rope_max_pos or (max_ctx_len + t_max)
+        stream = _lib.current_stream_handle(self.device)
+        self.rope = torch.empty((self.rope_max_pos, head_dim // 2, 2), dtype=torch.float32,
+                                device=self.device)
+        tree_attn_rope_table(head_dim, rope_base, self.rope_max_pos, self.rope, stream)
+        self.desc = make_desc(
+            batch=batch, t_max=t_max, num_heads=num_heads, num_kv_heads=num_kv_heads,
+            head_dim=head_dim, max_blocks_per_seq=max_blocks_per_seq, num_blocks=num_blocks,
+            max_ctx_len=max_ctx_len, dtype=TA_BF16 if dtype == torch.bfloat16 else TA_F32,
+            rope_table=self.rope, rope_max_pos=self.rope_max_pos, scale=scale, stream=stream,
+            flags=flags)
+        nbytes = tree_attn_workspace_size(self.desc)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.desc.workspace = self.workspace.data_ptr()
+        self.desc.workspace_bytes = self.workspace.numel()
+        tree_attn_workspace_init(self.desc)
+
+    def _sync_stream(self):
+        self.desc.stream = _lib.current_stream_handle(self.device)
+
+    def verify(self, q, k_new, v_new, kv_pages, block_table, ctx_lens, tree_parent, tree_depth,
+               out=None):
+        self._sync_stream()
+        if out is None:
+            out = torch.empty_like(q)
+        tree_attn_verify(self.desc, q, k_new, v_new, kv_pages, block_table, ctx_lens,
+                         tree_parent, tree_depth, out)
+        return out
+
+    def accept(self, node_argmax, cand_tokens, tree_parent, accept_len=None, accept_path=None):
+        self._sync_stream()
+        B, T = self.desc.batch, self.desc.t_max
+        if accept_len is None:
+            accept_len = torch.empty((B,), dtype=torch.int32, device=self.device)
+        if accept_path is None:
+            accept_path = torch.empty((B, T), dtype=torch.int32, device=self.device)
+        tree_accept_greedy(self.desc, node_argmax, cand_tokens, tree_parent, accept_len,
+                           accept_path)
+        return accept_len, accept_path
+
+    def commit(self, k_new, v_new, accept_len, accept_path, kv_pages, block_table, ctx_lens):
+        self._sync_stream()
+        kv_commit_path(self.desc, k_new, v_new, accept_len, accept_path, kv_pages, block_table,
+                       ctx_lens)

@@ -24,8 +24,10 @@ t_max carry parent -2.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -184,16 +186,31 @@ def draw_tokens(rng: np.random.Generator, parent: np.ndarray, vocab: int,
 
 # ----------------------------------------------------------- dense data ---
 
-def _normal(rng: np.random.Generator, shape, dtype: torch.dtype,
-            chunk_elems: int = 1 << 26) -> torch.Tensor:
-    """N(0,1) drawn in fp32, then rounded (RNE) to `dtype`, in chunks."""
+def _normal(seed_seq: np.random.SeedSequence, shape, dtype: torch.dtype,
+            chunk_elems: int = 1 << 24) -> torch.Tensor:
+    """N(0,1) drawn in fp32, then rounded (RNE) to `dtype`.  The tensor is cut
+    into fixed-size chunks, each drawn from its own spawned PCG64 stream, so
+    the values do not depend on how many threads fill it."""
     out = torch.empty(shape, dtype=dtype)
     flat = out.view(-1)
     n = flat.numel()
-    for s in range(0, n, chunk_elems):
+    starts = list(range(0, n, chunk_elems))
+    seqs = seed_seq.spawn(len(starts))
+
+    def fill(k):
+        s = starts[k]
         e = min(n, s + chunk_elems)
-        x = rng.standard_normal(e - s, dtype=np.float32)
+        g = np.random.Generator(np.random.PCG64(seqs[k]))
+        x = g.standard_normal(e - s, dtype=np.float32)
         flat[s:e] = torch.from_numpy(x).to(dtype)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(starts)))
+    if workers == 1:
+        for k in range(len(starts)):
+            fill(k)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(len(starts))))
     return out
 
 
@@ -202,6 +219,7 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
                   tree_sizes: Optional[tuple] = None,
                   max_depth: Optional[int] = None,
                   heads: Optional[int] = None,
+                  head_dim: Optional[int] = None,
                   chain: bool = False,
                   extra_pool_blocks: int = 0) -> Workload:
     """Build a seeded workload.  Keyword overrides shrink or reshape a preset
@@ -222,11 +240,13 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
     if heads is not None:
         repl["heads"] = heads
         repl["kv_heads"] = heads
+    if head_dim is not None:
+        repl["head_dim"] = head_dim
     if repl:
         spec = dataclasses.replace(spec, **repl)
     ss = np.random.SeedSequence([seed, 0x6D656475])
-    r_meta, r_q, r_k, r_v, r_pool = [np.random.Generator(np.random.PCG64(s))
-                                     for s in ss.spawn(5)]
+    s_meta, s_q, s_k, s_v, s_pool = ss.spawn(5)
+    r_meta = np.random.Generator(np.random.PCG64(s_meta))
     B, T = spec.batch, spec.t_max
     lo, hi = spec.ctx_range
     ctx = r_meta.integers(lo, hi + 1, size=B).astype(np.int32)
@@ -250,7 +270,8 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
     depth = np.stack([depths_of(parent[b]) for b in range(B)]).astype(np.int32)
     dmax = int(depth.max())
     per_seq = [math.ceil((int(ctx[b]) + dmax + 1) / BLOCK_SIZE) for b in range(B)]
-    max_blocks = max(per_seq)
+    # table columns cover the context bound plus one accepted path
+    max_blocks = max(max(per_seq), math.ceil((hi + dmax + 1) / BLOCK_SIZE))
     nblocks = sum(per_seq) + extra_pool_blocks
     perm = r_meta.permutation(nblocks).astype(np.int32)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
@@ -260,10 +281,10 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
         off += per_seq[b]
     tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
     H, Hkv, d = spec.heads, spec.kv_heads, spec.head_dim
-    q = _normal(r_q, (B, T, H, d), tdt)
-    k_new = _normal(r_k, (B, T, Hkv, d), tdt)
-    v_new = _normal(r_v, (B, T, Hkv, d), tdt)
-    pool = _normal(r_pool, (nblocks, 2, Hkv, BLOCK_SIZE, d), tdt)
+    q = _normal(s_q, (B, T, H, d), tdt)
+    k_new = _normal(s_k, (B, T, Hkv, d), tdt)
+    v_new = _normal(s_v, (B, T, Hkv, d), tdt)
+    pool = _normal(s_pool, (nblocks, 2, Hkv, BLOCK_SIZE, d), tdt)
     return Workload(spec=spec, seed=seed, ctx_lens=ctx, tree_sizes=sizes,
                     tree_parent=parent, tree_depth=depth, cand_tokens=cand,
                     node_argmax=amax, block_table=table, num_blocks=nblocks,

@@ -1,0 +1,166 @@
+"""C ABI checks that need no GPU.
+
+* The shared library loads and exports every function include/tree_attn.h
+  declares.
+* Every failure the host can detect returns its TA_ERR_* code before anything
+  is enqueued (these calls never reach the HIP runtime, so they run on a
+  machine without a GPU; no call here passes a descriptor and pointers that
+  would pass validation).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import medusa_tree_attention_attn_amd as ta
+from medusa_tree_attention_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from medusa_tree_attention_attn_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(_lib.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def _desc(**kw):
+    base = dict(batch=2, t_max=64, num_heads=4, num_kv_heads=4, head_dim=128,
+                max_blocks_per_seq=20, num_blocks=40, max_ctx_len=200, dtype=ta.TA_BF16,
+                rope_table=0x1000, rope_max_pos=264)
+    base.update(kw)
+    return ta.make_desc(**base)
+
+
+def _verify_rc(lib, desc, null_arg=None):
+    args = [0x2000 + 0x100 * i for i in range(9)]
+    if null_arg is not None:
+        args[null_arg] = None
+    return lib.tree_attn_verify(ctypes.byref(desc) if desc is not None else None, *args)
+
+
+def _commit_rc(lib, desc, null_arg):
+    args = [0x2000 + 0x100 * i for i in range(7)]
+    args[null_arg] = None
+    return lib.kv_commit_path(ctypes.byref(desc), *args)
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(t_max=65), -4),
+    (dict(t_max=0), -2),
+    (dict(batch=0), -2),
+    (dict(num_heads=0), -2),
+    (dict(num_blocks=0), -2),
+    (dict(max_ctx_len=-1), -2),
+    (dict(dtype=7), -3),
+    (dict(head_dim=96), -5),
+    (dict(num_heads=6, num_kv_heads=4), -6),
+    (dict(block_size=32), -7),
+    (dict(max_blocks_per_seq=12), -10),          # 12*16 < 200
+    (dict(rope_table=None), -9),
+    (dict(rope_max_pos=263), -9),
+])
+def test_descriptor_errors(lib, kw, code):
+    desc = _desc(**kw)
+    assert _verify_rc(lib, desc) == code
+    assert lib.tree_attn_workspace_size(ctypes.byref(desc)) == 0
+    assert _commit_rc(lib, desc, 0) == code
+
+
+def test_null_descriptor(lib):
+    assert lib.tree_attn_verify(None, *([None] * 9)) == -1
+    assert lib.tree_accept_greedy(None, *([None] * 5)) == -1
+    assert lib.kv_commit_path(None, *([None] * 7)) == -1
+    assert lib.tree_attn_workspace_size(None) == 0
+    assert lib.tree_attn_workspace_init(None) == -1
+
+
+@pytest.mark.parametrize("which", range(9))
+def test_verify_null_tensor(lib, which):
+    assert _verify_rc(lib, _desc(), null_arg=which) == -1
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_commit_null_tensor(lib, which):
+    assert _commit_rc(lib, _desc(), which) == -1
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_accept_null_and_dims(lib, which):
+    args = [0x3000 + 0x100 * i for i in range(5)]
+    args[which] = None
+    assert lib.tree_accept_greedy(ctypes.byref(_desc()), *args) == -1
+    good = [0x3000 + 0x100 * i for i in range(5)]
+    assert lib.tree_accept_greedy(ctypes.byref(_desc(t_max=65)), *good) == -4
+    assert lib.tree_accept_greedy(ctypes.byref(_desc(batch=0)), *good) == -2
+
+
+def test_workspace_requirement(lib):
+    desc = _desc()
+    need = lib.tree_attn_workspace_size(ctypes.byref(desc))
+    if need == 0:
+        pytest.skip("this descriptor takes a kernel without workspace")
+    desc.workspace = 0x5000
+    desc.workspace_bytes = need - 1
+    assert _verify_rc(lib, desc) == -8
+    desc.workspace = None
+    desc.workspace_bytes = need
+    assert _verify_rc(lib, desc) == -8
+
+
+def test_workspace_size_grows_with_context(lib):
+    a = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=200)))
+    b = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=4000, max_blocks_per_seq=260,
+                                                        rope_max_pos=4064)))
+    assert b >= a
+    simple = lib.tree_attn_workspace_size(ctypes.byref(_desc(flags=ta.TA_FLAG_SIMPLE_KERNEL)))
+    assert simple == 0
+    f32 = lib.tree_attn_workspace_size(ctypes.byref(_desc(dtype=ta.TA_F32)))
+    assert f32 == 0
+
+
+def test_rope_table_errors(lib):
+    assert lib.tree_attn_rope_table(128, 10000.0, 10, None, None) == -1
+    assert lib.tree_attn_rope_table(96, 10000.0, 10, 0x1000, None) == -5
+    assert lib.tree_attn_rope_table(128, 10000.0, 0, 0x1000, None) == -2
+    assert lib.tree_attn_rope_table(128, 1.0, 10, 0x1000, None) == -2
+
+
+def test_strerror_covers_every_code(lib):
+    for code in _lib.STATUS:
+        msg = _lib.strerror(code)
+        assert msg and msg != "unknown status"
+    assert _lib.strerror(-99) == "unknown status"
+
+
+def test_binding_raises_with_code(lib):
+    desc = _desc(t_max=65)
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.tree_attn_verify(desc, *[0x2000] * 9)
+    assert e.value.code == -4

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: accept_len, accept_path and the KV pool after commit are bit-exact;
+attention outputs are within max-abs 1e-2 of the fp64 oracle (bf16 or fp32
+inputs, fp32 accumulation, output rounded to the input dtype).  The RoPE
+table the library builds is bit-identical to the oracle's own.
+
+Sizes: the small presets run whole; the 16-sequence 7B preset runs whole for
+seed 0; the 13B and stress presets run at full size on the GPU and are checked
+on sampled sequences (sub-problems holding only the pages those sequences
+reference), chosen to include the longest and shortest contexts and every tree
+size of the stress mix.  Edge cases: empty context, single-node trees,
+contexts that end mid-page, padded (ragged) trees, chains reaching depth 63,
+grouped-query heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_workload
+from tests._helpers import dev, oracle_verify_rows, pool_bits, verifier
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+# `out` has q's dtype, so the result is rounded to bf16 after the fp32
+# accumulation: that rounding alone is up to 2^-8 * |out|, which exceeds 1e-2
+# once |out| > 2.56.  With contexts of >= 128 tokens (every preset workload)
+# |out| stays well below 1 and the plain 1e-2 bar is asserted; the edge cases
+# with a handful of keys (empty context) get the rounding term on top.
+RTOL_OUT_ROUNDING = 2.0 ** -8
+
+
+def _verify_gpu(wl, flags=0, max_ctx_len=None):
+    d = dev(wl)
+    tv = verifier(wl, flags=flags, max_ctx_len=max_ctx_len)
+    out = tv.verify(d["q"], d["k_new"], d["v_new"], d["kv_pages"], d["block_table"],
+                    d["ctx_lens"], d["tree_parent"], d["tree_depth"])
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _check_rows(got, ref, wl, seqs):
+    real = wl.tree_parent[seqs] != oracle.PAD_PARENT        # [len(seqs)][T]
+    err = np.abs(got - ref)
+    assert np.all(got[~real] == 0.0), "padding rows must be zero"
+    worst = float(err[real].max())
+    print(f"  max |gpu - oracle| = {worst:.3e}", flush=True)
+    if int(np.min(wl.ctx_lens[seqs])) >= 128:
+        assert worst <= ATOL, worst
+    else:
+        bound = ATOL + RTOL_OUT_ROUNDING * np.abs(ref)
+        assert np.all(err[real] <= bound[real]), float((err / bound)[real].max())
+
+
+FULL_CASES = [
+    ("tiny", s, {}) for s in range(5)
+] + [
+    ("vicuna7b_bs1", 0, {}),
+    ("vicuna7b_bs1", 1, {}),
+    ("vicuna7b_b16", 0, {}),
+    # several tiles and a ragged tail per sequence, small enough to check whole
+    ("vicuna7b_b16", 3, dict(batch=3, heads=4, ctx_range=(1, 1100))),
+    # empty contexts: the root attends only to itself
+    ("vicuna7b_b16", 4, dict(batch=2, heads=2, ctx_range=(0, 0))),
+    # contexts ending mid-page, trees of every stress size (ragged padding)
+    ("stress_b64", 5, dict(batch=8, heads=2, ctx_range=(1, 77))),
+    # single-node trees = plain paged decode
+    ("stress_b64", 6, dict(batch=4, heads=2, ctx_range=(100, 600), tree_sizes=(1,))),
+    # deep random trees (depth cap 63)
+    ("vicuna7b_bs1", 7, dict(batch=2, heads=2, ctx_range=(30, 300), tree_sizes=(64,),
+                             max_depth=63)),
+    # head_dim 64 in bf16
+    ("vicuna7b_b16", 14, dict(batch=3, heads=3, head_dim=64, ctx_range=(0, 500))),
+]
+
+
+@pytest.mark.parametrize("name,seed,kw", FULL_CASES,
+                         ids=[f"{n}-s{s}-{i}" for i, (n, s, _) in enumerate(FULL_CASES)])
+@pytest.mark.parametrize("kernel", ["default", "simple"])
+def test_verify_full(name, seed, kw, kernel):
+    wl = make_workload(name, seed, **kw)
+    flags = 1 if kernel == "simple" else 0
+    print(f"verify {name} seed={seed} {kw} kernel={kernel}", flush=True)
+    got = _verify_gpu(wl, flags)
+    ref = oracle_verify_rows(wl, range(wl.spec.batch))
+    _check_rows(got, ref, wl, list(range(wl.spec.batch)))
+
+
+def test_verify_chain_depth_63():
+    wl = make_workload("vicuna7b_bs1", 8, batch=2, heads=2, ctx_range=(17, 40),
+                       tree_sizes=(64,), chain=True)
+    got = _verify_gpu(wl)
+    ref = oracle_verify_rows(wl, [0, 1])
+    _check_rows(got, ref, wl, [0, 1])
+
+
+def _sample_seqs(wl, k):
+    order = np.argsort(wl.ctx_lens)
+    picks = {int(order[0]), int(order[-1])}
+    for t in sorted(set(wl.tree_sizes.tolist())):
+        picks.add(int(np.flatnonzero(wl.tree_sizes == t)[0]))
+    rng = np.random.default_rng(wl.seed)
+    while len(picks) < k:
+        picks.add(int(rng.integers(wl.spec.batch)))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name,seed,nseq,heads", [
+    ("vicuna7b_b16", 1, 6, [0, 7, 31]),
+    ("vicuna13b_b8", 0, 3, [0, 19, 39]),
+    ("stress_b64", 0, 8, [0, 13, 31]),
+])
+def test_verify_sampled_full_size(name, seed, nseq, heads):
+    wl = make_workload(name, seed)
+    print(f"verify full-size {name} seed={seed}", flush=True)
+    got = _verify_gpu(wl)
+    seqs = _sample_seqs(wl, nseq)
+    ref = oracle_verify_rows(wl, seqs, heads)
+    _check_rows(got[seqs][:, :, heads], ref, wl, seqs)
+
+
+def test_verify_grouped_query_heads():
+    wl = make_workload("vicuna7b_b16", 9, batch=2, heads=8, ctx_range=(50, 400))
+    # 8 query heads sharing 2 KV heads: keep every 4th KV head of the draw
+    kn = wl.k_new[:, :, ::4].contiguous()
+    vn = wl.v_new[:, :, ::4].contiguous()
+    pool = wl.kv_pages[:, :, ::4].contiguous()
+    import dataclasses
+    spec = dataclasses.replace(wl.spec, kv_heads=2)
+    wl = dataclasses.replace(wl, spec=spec, k_new=kn, v_new=vn, kv_pages=pool)
+    got = _verify_gpu(wl)
+    ref = oracle_verify_rows(wl, [0, 1])
+    _check_rows(got, ref, wl, [0, 1])
+
+
+def test_verify_is_deterministic():
+    wl = make_workload("vicuna7b_b16", 2, batch=4, heads=4, ctx_range=(200, 1500))
+    a = _verify_gpu(wl)
+    b = _verify_gpu(wl)
+    assert np.array_equal(a, b)
+
+
+def test_verify_larger_max_ctx_bound():
+    """The grid is sized by the host bound; a loose bound changes nothing."""
+    wl = make_workload("vicuna7b_b16", 10, batch=3, heads=2, ctx_range=(100, 900))
+    a = _verify_gpu(wl)
+    b = _verify_gpu(wl, max_ctx_len=wl.max_blocks * 16 - wl.spec.t_max)
+    assert np.max(np.abs(a - b)) <= 1e-6 or np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------- accept --
+
+def _accept_gpu(wl):
+    d = dev(wl)
+    tv = verifier(wl)
+    L, P = tv.accept(d["node_argmax"], d["cand_tokens"], d["tree_parent"])
+    torch.cuda.synchronize()
+    return L.cpu().numpy(), P.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "vicuna7b_bs1", "vicuna7b_b16", "vicuna13b_b8",
+                                  "stress_b64"])
+def test_accept_bit_exact(name):
+    for seed in range(5):
+        wl = make_workload(name, seed, heads=1, ctx_range=(16, 16))
+        L, P = _accept_gpu(wl)
+        Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+        assert np.array_equal(L, Lr) and np.array_equal(P, Pr), (name, seed)
+
+
+def test_accept_exhaustive_small_trees_on_gpu():
+    """Every tree with T <= 7 nodes x every edge-match pattern, as one batch
+    per T (duplicate sibling tokens included)."""
+    import itertools
+    from medusa_tree_attention_attn_amd import TreeVerifier
+    rng = np.random.default_rng(0)
+    for T in range(1, 8):
+        rows_p, rows_c, rows_a = [], [], []
+        for ps in itertools.product(*[range(i) for i in range(1, T)]):
+            par = [-1] + list(ps)
+            for pat in itertools.product([False, True], repeat=T - 1):
+                amax = rng.integers(100, 200, size=T)
+                cand = [0] + [int(amax[par[i]]) if pat[i - 1] else int(amax[par[i]]) + 1000
+                              for i in range(1, T)]
+                rows_p.append(par)
+                rows_c.append(cand)
+                rows_a.append(amax)
+        P = np.array(rows_p, dtype=np.int32)
+        C = np.array(rows_c, dtype=np.int32)
+        A = np.array(rows_a, dtype=np.int32)
+        B = P.shape[0]
+        tv = TreeVerifier(batch=B, t_max=T, num_heads=1, num_kv_heads=1, head_dim=64,
+                          max_blocks_per_seq=1, num_blocks=1, max_ctx_len=0,
+                          dtype=torch.float32)
+        g = lambda a: torch.from_numpy(a).cuda()
+        L, path = tv.accept(g(A), g(C), g(P))
+        torch.cuda.synchronize()
+        Lr, Pr = oracle.accept_greedy(A, C, P)
+        assert np.array_equal(L.cpu().numpy(), Lr), T
+        assert np.array_equal(path.cpu().numpy(), Pr), T
+
+
+def test_accept_all_and_none_match():
+    wl = make_workload("vicuna7b_b16", 11, heads=1, ctx_range=(16, 16))
+    for val in (0, 1):
+        amax = np.full_like(wl.node_argmax, 5)
+        cand = np.full_like(wl.cand_tokens, 5 + val)
+        import dataclasses
+        w2 = dataclasses.replace(wl, node_argmax=amax, cand_tokens=cand)
+        L, P = _accept_gpu(w2)
+        Lr, Pr = oracle.accept_greedy(amax, cand, wl.tree_parent)
+        assert np.array_equal(L, Lr) and np.array_equal(P, Pr)
+
+
+# ----------------------------------------------------------------- commit --
+
+def _commit_gpu(wl, L=None, P=None):
+    d = dev(wl)
+    tv = verifier(wl)
+    if L is None:
+        Lg, Pg = tv.accept(d["node_argmax"], d["cand_tokens"], d["tree_parent"])
+    else:
+        Lg = torch.from_numpy(L).cuda()
+        Pg = torch.from_numpy(P).cuda()
+    tv.commit(d["k_new"], d["v_new"], Lg, Pg, d["kv_pages"], d["block_table"], d["ctx_lens"])
+    torch.cuda.synchronize()
+    return d["kv_pages"], Lg.cpu().numpy(), Pg.cpu().numpy(), tv
+
+
+@pytest.mark.parametrize("name,seed,kw", [
+    ("tiny", 0, {}), ("tiny", 1, dict(ctx_range=(0, 31))),
+    ("vicuna7b_bs1", 0, {}), ("vicuna7b_b16", 0, {}), ("vicuna13b_b8", 0, {}),
+    ("stress_b64", 3, dict(batch=12, heads=4, ctx_range=(0, 200))),
+])
+def test_commit_bit_exact_whole_pool(name, seed, kw):
+    wl = make_workload(name, seed, **kw)
+    # force long accepted paths so every depth is exercised
+    amax = np.full_like(wl.node_argmax, 9)
+    cand = np.full_like(wl.cand_tokens, 9)
+    L, P = oracle.accept_greedy(amax, cand, wl.tree_parent)
+    pool_gpu, _, _, tv = _commit_gpu(wl, L, P)
+    rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
+    ref = oracle.commit(wl.k_new, wl.v_new, L, P, wl.kv_pages, wl.block_table, wl.ctx_lens, rope)
+    got = pool_bits(pool_gpu.cpu())
+    exp = pool_bits(ref)
+    diff = (got != exp).nonzero()
+    assert diff.numel() == 0, f"{diff.shape[0]} differing elements, first {diff[:4].tolist()}"
+
+
+def test_commit_stress_full_size():
+    wl = make_workload("stress_b64", 0)
+    before = wl.kv_pages.to("cuda")
+    pool_gpu, L, P, _ = _commit_gpu(wl)
+    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+    assert np.array_equal(L, Lr) and np.array_equal(P, Pr)
+    # touched pages: every page of the committed slots
+    touched = set()
+    for b in range(wl.spec.batch):
+        for i in range(int(L[b])):
+            touched.add(int(wl.block_table[b, (int(wl.ctx_lens[b]) + i) // 16]))
+    touched = sorted(touched)
+    idx = torch.tensor(touched, device="cuda")
+    mask = torch.ones(wl.num_blocks, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    assert torch.equal(pool_bits(pool_gpu[mask]), pool_bits(before[mask]))
+    # the touched pages against the oracle on the sub-problem
+    rope = oracle.rope_table(128, wl.max_ctx_len + wl.spec.t_max)
+    sub_pool = wl.kv_pages.index_select(0, torch.tensor(touched))
+    remap = {blk: k for k, blk in enumerate(touched)}
+    table = np.array([[remap.get(int(x), -1) for x in row] for row in wl.block_table],
+                     dtype=np.int32)
+    ref = oracle.commit(wl.k_new, wl.v_new, L, P, sub_pool, table, wl.ctx_lens, rope)
+    got = pool_gpu.index_select(0, idx).cpu()
+    assert torch.equal(pool_bits(got), pool_bits(ref))
+
+
+# ------------------------------------------------------------------- rope --
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_table_bit_exact(d):
+    from medusa_tree_attention_attn_amd import tree_attn_rope_table
+    n = 8192 + 64 + 64
+    t = torch.empty((n, d // 2, 2), dtype=torch.float32, device="cuda")
+    tree_attn_rope_table(d, 10000.0, n, t, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = t.cpu().numpy()
+    ref = oracle.rope_table(d, n)
+    bad = np.flatnonzero(got.view(np.uint32).ravel() != ref.view(np.uint32).ravel())
+    assert bad.size == 0, f"{bad.size} of {ref.size} table entries differ"
+
+
+# ------------------------------------------------------------- full step --
+
+def test_two_chained_steps_match_oracle():
+    """verify -> accept -> commit, then verify again at ctx + accept_len:
+    both verifies and the commit agree with the oracle run the same way."""
+    wl = make_workload("vicuna7b_b16", 12, batch=4, heads=4, ctx_range=(40, 700),
+                       tree_sizes=(30,))
+    d = dev(wl)
+    tv = verifier(wl, max_ctx_len=wl.max_ctx_len + wl.max_depth + 1)
+    out1 = tv.verify(d["q"], d["k_new"], d["v_new"], d["kv_pages"], d["block_table"],
+                     d["ctx_lens"], d["tree_parent"], d["tree_depth"])
+    L, P = tv.accept(d["node_argmax"], d["cand_tokens"], d["tree_parent"])
+    tv.commit(d["k_new"], d["v_new"], L, P, d["kv_pages"], d["block_table"], d["ctx_lens"])
+    ctx2 = d["ctx_lens"] + L
+    # second step reuses the tree but with fresh q/k/v draws
+    w2 = make_workload("vicuna7b_b16", 13, batch=4, heads=4, ctx_range=(40, 700),
+                       tree_sizes=(30,))
+    out2 = tv.verify(w2.q.cuda(), w2.k_new.cuda(), w2.v_new.cuda(), d["kv_pages"],
+                     d["block_table"], ctx2, d["tree_parent"], d["tree_depth"])
+    torch.cuda.synchronize()
+    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+    assert np.array_equal(L.cpu().numpy(), Lr) and np.array_equal(P.cpu().numpy(), Pr)
+    rope = oracle.rope_table(128, wl.max_ctx_len + wl.max_depth + 1 + wl.spec.t_max)
+    pool1 = oracle.commit(wl.k_new, wl.v_new, Lr, Pr, wl.kv_pages, wl.block_table,
+                          wl.ctx_lens, rope)
+    assert torch.equal(pool_bits(d["kv_pages"].cpu()), pool_bits(pool1))
+    r1 = oracle.verify(wl.q, wl.k_new, wl.v_new, wl.kv_pages, wl.block_table, wl.ctx_lens,
+                       wl.tree_parent, wl.tree_depth)
+    r2 = oracle.verify(w2.q, w2.k_new, w2.v_new, pool1, wl.block_table, wl.ctx_lens + Lr,
+                       wl.tree_parent, wl.tree_depth)
+    real = wl.tree_parent != oracle.PAD_PARENT
+    assert np.abs(out1.float().cpu().numpy() - r1)[real].max() <= ATOL
+    assert np.abs(out2.float().cpu().numpy() - r2)[real].max() <= ATOL
