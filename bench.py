@@ -1,0 +1,306 @@
+"""Benchmark of the Medusa tree-verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = tree_attn_verify -> tree_accept_greedy -> kv_commit_path over one
+batch of the synthetic workload (default: batch 16, 32 heads, head_dim 128,
+bf16, contexts uniform in [256, 2048], trees of 64 nodes of depth <= 4,
+acceptance probability 0.3).  W untimed steps, then exactly K timed steps
+between two device synchronisations.  Inputs are resident in HBM before the
+timed region; the steps rotate over enough copies of the inputs and of the KV
+pool (>= 1 GB in total) that the 256 MB Infinity Cache cannot serve a repeat.
+
+Prints one JSON line: verified tree-tokens/s (the outputs of the timed run
+are checked against the CPU oracle before anything is printed), the verify
+kernel's HBM roofline fraction from its HIP-event launch time and its
+algorithmic bytes, and the oracle timed on this host's CPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+POOL_BYTES_TARGET = 1 << 30
+
+
+def algorithmic_bytes(wl, accept_len=None):
+    """Bytes the step must move (per launch), from the workload's shapes:
+    verify: cached K/V of every context token, q + out + k_new + v_new of every
+    real node, block-table entries, tree metadata, RoPE rows of the distinct
+    positions; accept: argmax/candidates/parents + outputs; commit: the
+    accepted rows read from k_new/v_new and written to the pool."""
+    s = wl.spec
+    es = 2 if s.dtype == "bf16" else 4
+    ctx = wl.ctx_lens.astype(np.int64)
+    tb = wl.tree_sizes.astype(np.int64)
+    d, H, Hkv = s.head_dim, s.heads, s.kv_heads
+    kv = int((ctx * 2 * Hkv * d * es).sum())
+    qo = int((tb * 2 * H * d * es).sum())
+    kvn = int((tb * 2 * Hkv * d * es).sum())
+    table = int(((ctx + 15) // 16 * 4).sum())
+    meta = int((tb * 8).sum())
+    depth_rows = np.array([wl.tree_depth[b, : wl.tree_sizes[b]].max() + 1
+                           for b in range(s.batch)], dtype=np.int64)
+    rope = int((depth_rows * (d // 2) * 8).sum())
+    verify = kv + qo + kvn + table + meta + rope
+    accept = int((tb * 12).sum()) + s.batch * (4 + 4 * s.t_max)
+    commit = 0
+    if accept_len is not None:
+        commit = int((np.asarray(accept_len, dtype=np.int64) * 2 * Hkv * d * es * 2).sum())
+    return dict(verify=verify, accept=accept, commit=commit, kv=kv,
+                step=verify + accept + commit)
+
+
+def _i32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def parity_check(wl, out, L, P, pool_after, nseq=4):
+    """Outputs of the timed run against the CPU oracle: acceptance bit-exact
+    for the whole batch; attention within 1e-2 on sampled sequences (all
+    heads); committed rows bit-exact on those sequences' touched pages."""
+    import oracle
+    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+    ok_accept = np.array_equal(L, Lr) and np.array_equal(P, Pr)
+    order = np.argsort(wl.ctx_lens)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]),
+                   int(order[len(order) // 3])})[:nseq]
+    f = lambda t: t.to(torch.float32).numpy()
+    worst = 0.0
+    for b in seqs:
+        table = wl.block_table[[b]]
+        used = np.unique(table[table >= 0])
+        remap = -np.ones(wl.num_blocks, dtype=np.int64)
+        remap[used] = np.arange(len(used))
+        t2 = np.where(table >= 0, remap[np.maximum(table, 0)], -1).astype(np.int32)
+        sub_pool = f(wl.kv_pages.index_select(0, torch.from_numpy(used)))
+        q, kn, vn = f(wl.q[[b]]), f(wl.k_new[[b]]), f(wl.v_new[[b]])
+        real = wl.tree_parent[b] != oracle.PAD_PARENT
+        for h in range(wl.spec.heads):
+            ref = oracle.verify_head(q, kn, vn, sub_pool, t2, wl.ctx_lens[[b]],
+                                     wl.tree_parent[[b]], wl.tree_depth[[b]], 0, h)
+            worst = max(worst, float(np.abs(out[b, :, h].float().numpy() - ref)[real].max()))
+    # commit: the pages holding the accepted rows of the sampled sequences
+    rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
+    ok_commit = True
+    for b in seqs:
+        pages = sorted({int(wl.block_table[b, (int(wl.ctx_lens[b]) + i) // 16])
+                        for i in range(int(Lr[b]))})
+        sub = wl.kv_pages.index_select(0, torch.tensor(pages))
+        remap = {p: k for k, p in enumerate(pages)}
+        t2 = np.array([[remap.get(int(x), -1) for x in wl.block_table[b]]], dtype=np.int32)
+        ref = oracle.commit(wl.k_new[[b]], wl.v_new[[b]], Lr[[b]], Pr[[b]], sub, t2,
+                            wl.ctx_lens[[b]], rope)
+        got = pool_after.index_select(0, torch.tensor(pages))
+        ok_commit &= torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    return dict(accept_bit_exact=bool(ok_accept), commit_bit_exact=bool(ok_commit),
+                attn_max_abs_err=worst, sampled_sequences=seqs,
+                ok=bool(ok_accept and ok_commit and worst <= 1e-2))
+
+
+def cpu_baseline(wl):
+    """The oracle as it stands, one full step of this workload on one host
+    thread (BLAS limited to 1 thread), scaled to tree-tokens/s."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    f = lambda t: t.to(torch.float32).numpy()
+    q, kn, vn, pool = f(wl.q), f(wl.k_new), f(wl.v_new), f(wl.kv_pages)
+    rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
+    reps, dt = 0, 0.0
+    with threadpool_limits(1):
+        while reps < 4 and (reps == 0 or dt < 10.0):
+            t0 = time.perf_counter()
+            oracle.verify(q, kn, vn, pool, wl.block_table, wl.ctx_lens, wl.tree_parent,
+                          wl.tree_depth)
+            L, P = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+            oracle.commit(wl.k_new, wl.v_new, L, P, wl.kv_pages, wl.block_table, wl.ctx_lens,
+                          rope)
+            dt += time.perf_counter() - t0
+            reps += 1
+    return dict(value=round(reps * wl.tree_tokens / dt, 2), unit="tree-tokens/s", cores=1,
+                kind="oracle",
+                sample=f"{reps} full step(s) of the workload (verify of all {wl.spec.batch}x"
+                       f"{wl.spec.heads} (sequence, head) pairs, acceptance, commit), "
+                       f"seed {wl.seed}, {dt:.1f} s on 1 thread",
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vicuna7b_b16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain 512 MiB device copies (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the tree-verify step shards by sequence or head with no exchange; "
+              "multi-GPU runs are not part of it)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    from medusa_tree_attention_attn_amd import TreeVerifier
+    from synth import make_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    wl = make_workload(args.workload, args.seed)
+    s = wl.spec
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"workload {s.name} seed {args.seed}: generated in {time.perf_counter() - t_gen:.1f}s, "
+        f"{wl.tree_tokens} tree tokens, pool {wl.kv_pages.numel() * 2 / 1e6:.0f} MB")
+
+    pool_bytes = wl.kv_pages.numel() * wl.kv_pages.element_size()
+    copies = max(1, min(8, math.ceil(POOL_BYTES_TARGET / max(pool_bytes, 1))))
+    sets = []
+    for _ in range(copies):
+        sets.append(dict(q=wl.q.to(dev), k=wl.k_new.to(dev), v=wl.v_new.to(dev),
+                         pool=wl.kv_pages.to(dev), out=torch.empty_like(wl.q, device=dev)))
+    table, ctx = _i32(wl.block_table, dev), _i32(wl.ctx_lens, dev)
+    par, dep = _i32(wl.tree_parent, dev), _i32(wl.tree_depth, dev)
+    amax, cand = _i32(wl.node_argmax, dev), _i32(wl.cand_tokens, dev)
+    L = torch.empty((s.batch,), dtype=torch.int32, device=dev)
+    P = torch.empty((s.batch, s.t_max), dtype=torch.int32, device=dev)
+    tv = TreeVerifier(batch=s.batch, t_max=s.t_max, num_heads=s.heads, num_kv_heads=s.kv_heads,
+                      head_dim=s.head_dim, max_blocks_per_seq=wl.max_blocks,
+                      num_blocks=wl.num_blocks, max_ctx_len=wl.max_ctx_len,
+                      dtype=wl.torch_dtype, split_tokens=args.split_tokens)
+    log(f"{copies} rotating input copies ({copies * pool_bytes / 1e9:.2f} GB of KV pool), "
+        f"workspace {tv.workspace.numel() / 1e6:.1f} MB")
+
+    def verify(k):
+        st = sets[k % copies]
+        tv.verify(st["q"], st["k"], st["v"], st["pool"], table, ctx, par, dep, out=st["out"])
+
+    def step(k):
+        st = sets[k % copies]
+        verify(k)
+        tv.accept(amax, cand, par, L, P)
+        tv.commit(st["k"], st["v"], L, P, st["pool"], table, ctx)
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copies: 5 x 512 MiB device-to-device")
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    # Verify-kernel launch time for the roofline: the same launches back to
+    # back on the library's stream (torch's current stream) between two
+    # events, so event and launch overheads are amortised; rocprofv3's
+    # per-dispatch duration of the same command agrees with it.
+    nv = max(args.steps, 20)
+    torch.cuda.synchronize()
+    va = torch.cuda.Event(enable_timing=True)
+    vb = torch.cuda.Event(enable_timing=True)
+    va.record()
+    for k in range(nv):
+        verify(k)
+    vb.record()
+    torch.cuda.synchronize()
+    v_avg = va.elapsed_time(vb) / nv
+    # restore the outputs of the step loop's last step for the parity check
+    step(args.warmup + args.steps - 1)
+    torch.cuda.synchronize()
+
+    # parity of the timed run's outputs (last copy used by the last step)
+    last = sets[(args.warmup + args.steps - 1) % copies]
+    chk = parity_check(wl, last["out"].cpu(), L.cpu().numpy(), P.cpu().numpy(),
+                       last["pool"].cpu())
+    log(f"parity of timed outputs: {chk}")
+    if not chk["ok"]:
+        print(json.dumps({"metric": "verified tree-tokens/s", "error": "parity failed",
+                          "parity": chk}))
+        sys.exit(1)
+
+    nbytes = algorithmic_bytes(wl, L.cpu().numpy())
+    achieved = nbytes["verify"] / (v_avg * 1e-3) / 1e9
+    tokens_per_s = wl.tree_tokens / (ms_per_step * 1e-3)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl)
+        log(f"cpu baseline: {cpu}")
+        cpu.pop("seconds", None)
+    result = {
+        "metric": "verified tree-tokens/s (verify+accept+commit step)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{s.name}: batch {s.batch}, {s.heads} heads, head_dim {s.head_dim}, "
+                        f"{s.dtype}, contexts U[{s.ctx_range[0]},{s.ctx_range[1]}], trees of "
+                        f"{'/'.join(map(str, s.tree_sizes))} nodes, depth <= {s.max_depth}, "
+                        f"match p={s.p_match}, seed {args.seed}",
+            "global_batch": s.batch,
+            "tree_tokens_per_step": wl.tree_tokens,
+            "mean_ctx": float(wl.ctx_lens.mean()),
+            "split_tokens": tv.desc.split_tokens or "auto",
+            "rotating_copies": copies,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "verify_mfma_kernel" + (" + combine_kernel" if tv.workspace_bytes_needed else ""),
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": nbytes["verify"],
+            "avg_launch_us": round(v_avg * 1e3, 2),
+        },
+        "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "parity": {k: chk[k] for k in ("accept_bit_exact", "commit_bit_exact",
+                                       "attn_max_abs_err")},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,7 @@
  * Conventions shared by every call
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
- *    contiguous.  The library allocates nothing, keeps no global state, never
+ *    contiguous, 16-byte aligned (the kernels move 16-byte vectors).  The library allocates nothing, keeps no global state, never
  *    synchronises the device with the host, and enqueues all work on
  *    desc->stream (a hipStream_t; NULL = the default stream).
  *  - Element type of q, k_new, v_new, kv_pages and out is desc->dtype
@@ -91,7 +91,8 @@ enum ta_status {
   TA_ERR_WORKSPACE = -8,      /* workspace NULL or smaller than required     */
   TA_ERR_ROPE_TABLE = -9,     /* rope table missing or rope_max_pos too small*/
   TA_ERR_CAPACITY = -10,      /* max_blocks_per_seq*16 < max_ctx_len         */
-  TA_ERR_LAUNCH = -11         /* the HIP runtime rejected a launch           */
+  TA_ERR_LAUNCH = -11,        /* the HIP runtime rejected a launch           */
+  TA_ERR_ALIGNMENT = -12      /* a tensor pointer is not 16-byte aligned     */
 };
 
 typedef struct tree_attn_desc {
@@ -113,6 +114,10 @@ typedef struct tree_attn_desc {
   size_t workspace_bytes;     /* its size, >= tree_attn_workspace_size(desc)  */
   void* stream;               /* hipStream_t                                  */
   int32_t flags;              /* enum ta_flags, 0 by default                  */
+  int32_t split_tokens;       /* context tokens per split-KV work item of the */
+                              /* MFMA kernel, rounded up to a multiple of 64  */
+                              /* and capped at 4096; 0 = chosen from batch,   */
+                              /* heads and max_ctx_len                        */
 } tree_attn_desc;
 
 /* Tree attention (vLLM #1171: several new tokens over a paged KV cache under
@@ -128,9 +133,9 @@ typedef struct tree_attn_desc {
  *                  . keys) . values, accumulated in fp32 and rounded to
  *                  dtype (round to nearest even).
  * Padding rows of out are written as zeros.  kv_pages is only read.
- * Needs desc->workspace of tree_attn_workspace_size(desc) bytes that was
- * zero-filled once (tree_attn_workspace_init); every call leaves it zeroed
- * again.  Errors: every TA_ERR_* code. */
+ * Needs desc->workspace of tree_attn_workspace_size(desc) bytes (its
+ * contents need no initialisation; it holds split-KV partials between the
+ * two kernels of one call).  Errors: every TA_ERR_* code. */
 int tree_attn_verify(const tree_attn_desc* desc, const void* q, const void* k_new,
                      const void* v_new, const void* kv_pages,
                      const int32_t* block_table, const int32_t* ctx_lens,
@@ -171,7 +176,8 @@ int kv_commit_path(const tree_attn_desc* desc, const void* k_new, const void* v_
 size_t tree_attn_workspace_size(const tree_attn_desc* desc);
 
 /* Zero-fills desc->workspace (desc->workspace_bytes bytes) on desc->stream
- * with a fill kernel.  Call once after allocating a workspace. */
+ * with a fill kernel.  Optional: tree_attn_verify does not need a cleared
+ * workspace. */
 int tree_attn_workspace_init(const tree_attn_desc* desc);
 
 /* Fills table[pos][k][0..1] = (cos, sin)(pos * base^(-2k/head_dim)) for

@@ -29,7 +29,7 @@ STATUS = {
     0: "TA_OK", -1: "TA_ERR_NULL_POINTER", -2: "TA_ERR_BAD_DIMS", -3: "TA_ERR_DTYPE",
     -4: "TA_ERR_TREE_TOO_LARGE", -5: "TA_ERR_HEAD_DIM", -6: "TA_ERR_HEADS",
     -7: "TA_ERR_BLOCK_SIZE", -8: "TA_ERR_WORKSPACE", -9: "TA_ERR_ROPE_TABLE",
-    -10: "TA_ERR_CAPACITY", -11: "TA_ERR_LAUNCH",
+    -10: "TA_ERR_CAPACITY", -11: "TA_ERR_LAUNCH", -12: "TA_ERR_ALIGNMENT",
 }
 EXPORTED = (
     "tree_attn_verify", "tree_accept_greedy", "kv_commit_path",
@@ -57,6 +57,7 @@ class TreeAttnDesc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("flags", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32),
     ]
 
 
@@ -124,7 +125,7 @@ def current_stream_handle(device=None) -> int:
 def make_desc(*, batch, t_max, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
               num_blocks, max_ctx_len, dtype, rope_table=None, rope_max_pos=0,
               workspace=None, workspace_bytes=0, scale=0.0, stream=None, flags=0,
-              block_size=16) -> TreeAttnDesc:
+              block_size=16, split_tokens=0) -> TreeAttnDesc:
     d = TreeAttnDesc()
     d.batch, d.t_max = batch, t_max
     d.num_heads, d.num_kv_heads, d.head_dim = num_heads, num_kv_heads, head_dim
@@ -138,6 +139,7 @@ def make_desc(*, batch, t_max, num_heads, num_kv_heads, head_dim, max_blocks_per
     d.workspace_bytes = workspace_bytes
     d.stream = stream
     d.flags = flags
+    d.split_tokens = split_tokens
     return d
 
 

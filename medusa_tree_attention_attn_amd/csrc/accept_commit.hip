@@ -60,7 +60,40 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ 
 // takes node n = accept_path[i] to position p = ctx_len + i: page
 // block_table[p / 16], row p % 16.  K is rotated at p with the fixed-order
 // fp32 arithmetic and rounded to the pool type; V is copied bit for bit.
+// Each thread handles 8 consecutive RoPE pairs with 16-byte loads, all issued
+// before any use, so a slot costs about one memory round trip.
 // ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16_to_f32((uint16_t)(u[j] & 0xFFFFu));
+    x[2 * j + 1] = bf16_to_f32((uint16_t)(u[j] >> 16));
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0], b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[4 + j] = b[j];
+  }
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&y)[8]) {
+  u32x4 u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    u[j] = (uint32_t)f32_to_bf16_rne(y[2 * j]) | ((uint32_t)f32_to_bf16_rne(y[2 * j + 1]) << 16);
+  *reinterpret_cast<u32x4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float (&y)[8]) {
+  reinterpret_cast<f32x4*>(p)[0] = f32x4{y[0], y[1], y[2], y[3]};
+  reinterpret_cast<f32x4*>(p)[1] = f32x4{y[4], y[5], y[6], y[7]};
+}
+
 template <typename S>
 __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   const int i = blockIdx.x, b = blockIdx.y;
@@ -74,23 +107,36 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   const int blk = p.block_table[(size_t)b * p.max_blocks + lb];
   if (blk < 0 || blk >= p.num_blocks) return;
   const int slot = pos % kPage;
-  const int D = p.D, half = p.D / 2;
+  const int D = p.D, half = p.D / 2, groups = half / 8;
   const S* kn = static_cast<const S*>(p.k_new) + ((size_t)b * p.T + n) * p.Hkv * D;
   const S* vn = static_cast<const S*>(p.v_new) + ((size_t)b * p.T + n) * p.Hkv * D;
   S* pages = static_cast<S*>(p.kv_pages);
   const float* cs = p.rope + (size_t)pos * D;
-  for (int idx = threadIdx.x; idx < p.Hkv * half; idx += blockDim.x) {
-    const int hk = idx / half, k = idx % half;
-    float y1, y2;
-    rope_pair_exact(ld(kn, (size_t)hk * D + k), ld(kn, (size_t)hk * D + k + half), cs[2 * k],
-                    cs[2 * k + 1], y1, y2);
+  for (int c = threadIdx.x; c < p.Hkv * groups; c += blockDim.x) {
+    const int hk = c / groups, k0 = (c % groups) * 8;
+    float x1[8], x2[8], cc[8], ss[8], y1[8], y2[8];
+    load8(kn + (size_t)hk * D + k0, x1);
+    load8(kn + (size_t)hk * D + k0 + half, x2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 t = reinterpret_cast<const f32x4*>(cs + 2 * k0)[j];
+      cc[2 * j] = t[0];
+      ss[2 * j] = t[1];
+      cc[2 * j + 1] = t[2];
+      ss[2 * j + 1] = t[3];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rope_pair_exact(x1[j], x2[j], cc[j], ss[j], y1[j], y2[j]);
     S* krow = pages + page_row(blk, 0, hk, slot, p.Hkv, D);
-    st(krow, k, y1);
-    st(krow, k + half, y2);
+    store8(krow + k0, y1);
+    store8(krow + k0 + half, y2);
   }
-  for (int idx = threadIdx.x; idx < p.Hkv * D; idx += blockDim.x) {
-    const int hk = idx / D, k = idx % D;
-    pages[page_row(blk, 1, hk, slot, p.Hkv, D) + k] = vn[(size_t)hk * D + k];
+  constexpr int kPer16 = 16 / sizeof(S);
+  const int row_chunks = D / kPer16;
+  for (int c = threadIdx.x; c < p.Hkv * row_chunks; c += blockDim.x) {
+    const int hk = c / row_chunks, off = (c % row_chunks) * kPer16;
+    *reinterpret_cast<u32x4*>(pages + page_row(blk, 1, hk, slot, p.Hkv, D) + off) =
+        *reinterpret_cast<const u32x4*>(vn + (size_t)hk * D + off);
   }
 }
 

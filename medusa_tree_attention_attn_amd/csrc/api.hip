@@ -29,6 +29,8 @@ int check_common(const tree_attn_desc* d) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_LAUNCH; }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -58,6 +60,10 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   const Plan plan = make_plan(*d);
   if (plan.bytes > 0 && (!d->workspace || d->workspace_bytes < plan.bytes))
     return TA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_pages) ||
+      !aligned16(out) || !aligned16(d->rope_cos_sin) ||
+      (plan.bytes > 0 && !aligned16(d->workspace)))
+    return TA_ERR_ALIGNMENT;
 
   VerifyParams p{};
   p.q = q;
@@ -85,7 +91,6 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
   if (plan.mfma) {
     char* ws = static_cast<char*>(d->workspace);
-    p.ws_count = reinterpret_cast<int32_t*>(ws + plan.off_count);
     p.ws_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
     p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
     return status_of(launch_verify_mfma(p, stream));
@@ -114,6 +119,9 @@ int kv_commit_path(const tree_attn_desc* d, const void* k_new, const void* v_new
   if (!k_new || !v_new || !accept_len || !accept_path || !kv_pages || !block_table ||
       !ctx_lens)
     return TA_ERR_NULL_POINTER;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_pages) ||
+      !aligned16(d->rope_cos_sin))
+    return TA_ERR_ALIGNMENT;
   CommitParams p{};
   p.k_new = k_new;
   p.v_new = v_new;
@@ -157,6 +165,7 @@ const char* tree_attn_strerror(int status) {
     case TA_ERR_ROPE_TABLE: return "rope table missing or rope_max_pos < max_ctx_len + t_max";
     case TA_ERR_CAPACITY: return "max_blocks_per_seq * 16 < max_ctx_len";
     case TA_ERR_LAUNCH: return "kernel launch failed";
+    case TA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
     default: return "unknown status";
   }
 }

@@ -12,8 +12,8 @@ namespace ta {
 // bf16 or fp32.  Plain and slow; no workspace.
 hipError_t launch_verify_simple(const VerifyParams& p, int dtype, hipStream_t stream);
 
-// MFMA split-KV kernel for bf16, head_dim 128, with the split combine fused
-// into the last-arriving work item of each (sequence, head).
+// MFMA split-KV kernel for bf16, head_dim 128, followed (when a context can
+// take more than one split) by the kernel that merges the split partials.
 hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream);
 
 hipError_t launch_accept(const int32_t* node_argmax, const int32_t* cand_tokens,

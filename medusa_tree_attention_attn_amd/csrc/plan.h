@@ -8,21 +8,23 @@
 
 namespace ta {
 
-// Context tokens per split work item of the MFMA kernel.  Long contexts are
-// cut into chunks of this many tokens so that every CU gets similar work;
-// a (sequence, head) whose context fits in one chunk writes `out` directly
-// and touches no workspace.
-constexpr int kChunkTokens = 512;
-
-// Set once the MFMA kernel is in place; until then every call takes the
-// plain kernel.
-constexpr bool kMfmaKernelReady = false;
+// Split-KV sizing of the MFMA kernel.  A (sequence, head) whose context fits
+// in one split is one work item and writes `out` directly; longer contexts
+// are cut into splits of `chunk` tokens (a multiple of the 64-token tile)
+// whose partials a second kernel merges.  Each work item pays a prologue
+// (tree rows, q and tree k/v rows, RoPE rows, first tile) before it streams,
+// and each split costs a partial write and read, so the plan splits only as
+// far as needed to give every CU two resident work items (kTargetItems), and
+// never below kMinChunk tokens.
+constexpr int kTargetItems = 512;
+constexpr int kMinChunk = 256;
+constexpr int kTileTokens = 64;
+constexpr int kMaxSplitTokens = 4096;   // the kernel keeps a split's page ids in LDS
 
 struct Plan {
   bool mfma;         // MFMA kernel (bf16, head_dim 128) or the plain kernel
   int chunk;         // tokens per split
   int splits;        // max splits per (sequence, head)
-  size_t off_count;  // int32 [B][H] arrival counters
   size_t off_ml;     // float2 [B][H][splits][T] (running max, running sum)
   size_t off_o;      // float [B][H][splits][T][128] un-normalised partial O
   size_t bytes;      // total workspace
@@ -32,14 +34,26 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline Plan make_plan(const tree_attn_desc& d) {
   Plan p{};
-  p.mfma = kMfmaKernelReady && d.dtype == TA_BF16 && d.head_dim == 128 && !(d.flags & TA_FLAG_SIMPLE_KERNEL);
-  p.chunk = kChunkTokens;
-  p.splits = d.max_ctx_len <= 0 ? 1 : (d.max_ctx_len + kChunkTokens - 1) / kChunkTokens;
-  if (!p.mfma) return p;
+  p.mfma = d.dtype == TA_BF16 && d.head_dim == 128 && !(d.flags & TA_FLAG_SIMPLE_KERNEL);
+  const int max_ctx = d.max_ctx_len > 0 ? d.max_ctx_len : 1;
+  int chunk;
+  if (d.split_tokens > 0) {
+    chunk = d.split_tokens;
+  } else {
+    const long long bh = (long long)d.batch * d.num_heads;
+    const long long want = (kTargetItems + bh - 1) / bh;
+    const int splits = (int)(want < 1 ? 1 : (want > max_ctx ? max_ctx : want));
+    chunk = (max_ctx + splits - 1) / splits;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+  }
+  chunk = (chunk + kTileTokens - 1) / kTileTokens * kTileTokens;
+  if (chunk > kMaxSplitTokens) chunk = kMaxSplitTokens;
+  p.chunk = chunk;
+  p.splits = (max_ctx + chunk - 1) / chunk;
+  if (!p.mfma || p.splits == 1) return p;  // no partials: no workspace
   const size_t bh = (size_t)d.batch * d.num_heads;
   const size_t rows = bh * (size_t)p.splits * d.t_max;
-  p.off_count = 0;
-  p.off_ml = align256(bh * sizeof(int32_t));
+  p.off_ml = 0;
   p.off_o = p.off_ml + align256(rows * 8);
   p.bytes = p.off_o + align256(rows * (size_t)d.head_dim * sizeof(float));
   return p;

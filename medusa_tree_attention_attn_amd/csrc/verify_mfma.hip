@@ -1,12 +1,616 @@
-// MFMA split-KV tree-verify kernel (bf16, head_dim 128) - under construction.
+// Tree-verify attention on gfx950 matrix cores (bf16, head_dim 128).
+//
+// What it computes is defined in tree_attn.h: every tree node attends to the
+// sequence's paged KV cache plus its own ancestors, RoPE at ctx_len + depth
+// (vLLM issue #1171: several new tokens over a paged cache under a tree mask;
+// TensorRT-LLM issue #1946: position offsets; LMDeploy PR #1231: TreeMask over
+// split-KV Flash Decoding).
+//
+// Work item = (sequence b, query head h, context split sp); one workgroup of
+// four wavefronts per item.  The split's context is streamed in tiles of 64
+// tokens (four 16-token pages):
+//   * each tile is loaded from HBM once, with 16-byte fully coalesced loads,
+//     into registers one tile ahead, then written to an LDS double buffer;
+//     every tree query of the head reads it from LDS;
+//   * wavefront (qt, th) owns query rows 32*qt .. 32*qt+31 (the tree nodes)
+//     and the 32-token half th of each tile;
+//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query
+//     column, so the softmax row statistics are lane-local (plus one exchange
+//     between the two lane halves), and P^T feeds the PV product's B operand
+//     straight from the accumulators;
+//   * V is transposed in registers on its way into LDS, with the tokens of
+//     each 16-token block permuted so that a lane's PV A operand is one
+//     16-byte read;
+//   * online softmax in base 2 (q is pre-scaled by scale*log2 e); the running
+//     max only moves when a tile's max exceeds it by more than 8, which skips
+//     most rescales of the output accumulators;
+//   * split 0 also processes the tree block: the T new keys, rotated with the
+//     fixed-order fp32 arithmetic and rounded to bf16 exactly as the commit
+//     will store them, masked by per-node ancestor bitmasks built with
+//     pointer doubling across the lanes of a wavefront.
+// Splits of one (b, h) leave (m, l, O) partials in the workspace; a second,
+// small kernel merges them.  The prologue takes two dependent memory round
+// trips: everything that does not depend on ctx_len (tree rows, q row, tree
+// k/v rows, page ids), then the (cos, sin) rows and the first context tile.
 #include "launch.h"
+#include "plan.h"
 
 namespace ta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+constexpr int kD = 128;
+constexpr int kTile = 64;                       // tokens per LDS tile (four pages)
+constexpr int kThreads = 256;
+// LDS tiles are row-major (one token per row) with padded rows: 16 lanes that
+// read one 16-byte chunk from 16 consecutive K rows, or one 64-bit transpose
+// read from 4 consecutive V rows x 32 bytes, land in distinct banks, and every
+// access is a lane-constant address plus an immediate offset.
+constexpr int kKRow = 256 + 16;
+constexpr int kVRow = 256 + 32;
+constexpr int kKBytes = kTile * kKRow;
+constexpr int kVBytes = kTile * kVRow;
+constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kSlack = 8.0f;                  // log2 units: p <= 2^8 before a rescale
+constexpr int kMaxSplitPages = kMaxSplitTokens / kPage;
+
+// Pipeline depth (context tiles in flight per workgroup) and the occupancy
+// the register budget is sized for (workgroups of 4 wavefronts per CU).
+#ifndef TA_PREFETCH_TILES
+#define TA_PREFETCH_TILES 1
+#endif
+#ifndef TA_WG_PER_CU
+#define TA_WG_PER_CU 2
+#endif
+constexpr int kDepth = TA_PREFETCH_TILES;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+__device__ __forceinline__ f32x16 mfma(const u32x4& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// gfx950 transpose read: within each group of 16 lanes, lane a points at four
+// consecutive 16-bit values E[a][0..3]; lane i receives E[4k + i/4][i%4] for
+// k = 0..3.  With lane a = 4k + r pointing at row (t0 + k), columns
+// d0 + 4r .. d0 + 4r + 3 of a row-major tile, lane i gets column d0 + i of
+// rows t0 .. t0+3: a column slice of V, as the PV operand needs it.
+__device__ __forceinline__ v4i16 ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+}
+
+// One tile's worth of global data held by a thread between load and store:
+// row tid/16 (of page p), 16-byte chunk tid%16, of the K and of the V plane.
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+// Where the split's pages live: their physical ids were copied into LDS
+// (s_pages[i] = page of tokens c0 + 16 i, -1 when absent or out of range) so
+// the tile loop issues its KV loads without waiting on any table lookup.
+struct Geo {
+  const uint16_t* pages;
+  const int* s_pages;
+  int c0, hk, Hkv;
+};
+
+// Issue the loads of context tile [tile0, tile0 + 64); pages at or beyond c1
+// are never loaded (their rows hold zeros and are masked).  Page ids are
+// uniform, so page addresses are scalar; each lane adds a constant offset.
+__device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int tile0, int c1,
+                                              int tid) {
+  const int pg0 = (tile0 - G.c0) >> 4;
+  const int off = (tid >> 4) * kD + (tid & 15) * 8;
+  const size_t v_plane = (size_t)G.Hkv * kPage * kD;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int blk =
+        tile0 + 16 * p < c1 ? __builtin_amdgcn_readfirstlane(G.s_pages[pg0 + p]) : -1;
+    if (blk >= 0) {
+      const uint16_t* kp = G.pages + page_row(blk, 0, G.hk, 0, G.Hkv, kD);
+      R.k[p] = *reinterpret_cast<const u32x4*>(kp + off);
+      R.v[p] = *reinterpret_cast<const u32x4*>(kp + v_plane + off);
+    } else {
+      R.k[p] = u32x4{0u, 0u, 0u, 0u};
+      R.v[p] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs& R, char* stage, int tid) {
+  char* kb = stage + (tid >> 4) * kKRow + (tid & 15) * 16;
+  char* vb = stage + kKBytes + (tid >> 4) * kVRow + (tid & 15) * 16;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    *reinterpret_cast<u32x4*>(kb + 16 * p * kKRow) = R.k[p];
+    *reinterpret_cast<u32x4*>(vb + 16 * p * kVRow) = R.v[p];
+  }
+}
+
+struct WaveState {
+  f32x16 o[4];  // O^T, d tiles of 32: lane owns query column, rows = d
+  float m, l;   // running max (log2 units) and this lane half's running sum
+};
+
+// Lane-constant LDS offsets of wavefront (qt, th) inside a stage.
+struct LaneOffs {
+  int k;   // K operand: row 32*th + lane%32, chunk lane/32 (+32 bytes per k-step)
+  int v;   // V transpose read: see ds_read_tr
+  int base;
+  int g;
+};
+
+__device__ __forceinline__ LaneOffs lane_offsets(int lane, int th) {
+  LaneOffs L;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int grp = lane >> 4, a = lane & 15;
+  L.base = 32 * th;
+  L.g = g;
+  L.k = (L.base + r32) * kKRow + g * 16;
+  L.v = kKBytes + (L.base + 4 * (grp >> 1) + (a >> 2)) * kVRow + (16 * (grp & 1) + 4 * (a & 3)) * 2;
+  return L;
+}
+
+enum TileMode { kFull = 0, kPartial = 1, kTreeTile = 2 };
+
+// One 64-token tile for wavefront (qt, th): tokens 32*th .. 32*th+31.
+template <int kMode>
+__device__ __forceinline__ void compute_tile(WaveState& st, const u32x4 (&qf)[8],
+                                             const char* stage, const LaneOffs& L, int n_valid,
+                                             uint64_t anc_q) {
+  f32x16 s = {};
+  const char* kp = stage + L.k;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    s = mfma(*reinterpret_cast<const u32x4*>(kp + 32 * ks), qf[ks], s);
+  if (kMode != kFull) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tt = L.base + 8 * (r >> 2) + 4 * L.g + (r & 3);
+      const bool ok = kMode == kTreeTile ? ((anc_q >> tt) & 1ull) != 0ull : tt < n_valid;
+      s[r] = ok ? s[r] : -INFINITY;
+    }
+  }
+  float tmax = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = (tmax > st.m + kSlack) ? tmax : st.m;
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  f32x8 p0, p1;
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    p0[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
+    p1[r] = __builtin_amdgcn_exp2f(s[r + 8] - m_use);
+    psum += p0[r] + p1[r];
+  }
+  st.l = st.l * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
+  }
+  st.m = m_new;
+  const bf16x8 pk[2] = {__builtin_convertvector(p0, bf16x8), __builtin_convertvector(p1, bf16x8)};
+  const char* vp = stage + L.v;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const v4i16 lo = ds_read_tr(vp + (16 * ks) * kVRow + 64 * dt);
+      const v4i16 hi = ds_read_tr(vp + (16 * ks + 8) * kVRow + 64 * dt);
+      const v8i16 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ks],
+                                                          st.o[dt], 0, 0, 0);
+    }
+}
+
+// Q^T fragments of query row q for k-steps 0..7 (chunk 2*ks + g), rotated at
+// pos and pre-scaled by scale*log2 e.  Chunk c and chunk c+8 hold the RoPE
+// partners d and d+64, so the rotation stays inside the lane.  Loaded in two
+// steps so that the row and its (cos, sin) table row travel in different
+// round trips of the prologue.
+struct QRaw {
+  u32x4 x[8];   // x[s] = chunk 2s+g (d < 64), x[4+s] = chunk 2s+g+8
+};
+struct QRope {
+  f32x4 t[16];  // t[4s + j2] = (cos, sin) of k = 8(2s+g) + 2 j2 and k+1
+};
+__device__ __forceinline__ void load_q_raw(QRaw& Q, const uint16_t* qrow, int g) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    Q.x[s] = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * s + g));
+    Q.x[4 + s] = *reinterpret_cast<const u32x4*>(qrow + 64 + 8 * (2 * s + g));
+  }
+}
+__device__ __forceinline__ void load_q_rope(QRope& Rq, const float* cs, int g) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2)
+      Rq.t[4 * s + j2] = reinterpret_cast<const f32x4*>(cs + 2 * 8 * (2 * s + g))[j2];
+}
+__device__ __forceinline__ void rotate_q(u32x4 (&qf)[8], const QRaw& Q, const QRope& Rq,
+                                         float qscale) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    f32x8 y1, y2;
+#pragma unroll
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const f32x4 t4 = Rq.t[4 * s + j2];
+      const float a0 = bf16_lo(Q.x[s][j2]), a1 = bf16_hi(Q.x[s][j2]);
+      const float b0 = bf16_lo(Q.x[4 + s][j2]), b1 = bf16_hi(Q.x[4 + s][j2]);
+      y1[2 * j2] = (a0 * t4[0] - b0 * t4[1]) * qscale;
+      y2[2 * j2] = (b0 * t4[0] + a0 * t4[1]) * qscale;
+      y1[2 * j2 + 1] = (a1 * t4[2] - b1 * t4[3]) * qscale;
+      y2[2 * j2 + 1] = (b1 * t4[2] + a1 * t4[3]) * qscale;
+    }
+    qf[s] = __builtin_bit_cast(u32x4, __builtin_convertvector(y1, bf16x8));
+    qf[s + 4] = __builtin_bit_cast(u32x4, __builtin_convertvector(y2, bf16x8));
+  }
+}
+
+// The tree block as a 64-token tile: key j = RoPE(k_new[b][j], ctx+depth[j])
+// with the commit's fixed-order fp32 arithmetic, rounded to bf16 as stored;
+// value j = v_new[b][j].  Nodes >= t_real are zero.  Thread tid rotates node
+// tid/4, dims 16*(tid%4) .. +15 and their partners; it copies V rows
+// 16*q4 + tid/16, chunk tid%16.
+struct TreeRaw {
+  u32x4 k[4];    // chunks 2u, 2u+1 (first half) and 8+2u, 9+2u (second half)
+  u32x4 v[4];
+  f32x4 cs[8];   // (cos, sin) of k = 16u .. 16u+15
+};
+__device__ __forceinline__ void load_tree_raw(TreeRaw& TR, const VerifyParams& p, int b, int hk,
+                                              int t_real_hint, int tid) {
+  const int T = p.T;
+  const uint16_t* kn = static_cast<const uint16_t*>(p.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(p.v_new);
+  const int j = tid >> 2, u = tid & 3;
+  if (j < t_real_hint) {
+    const uint16_t* row = kn + (((size_t)b * T + j) * p.Hkv + hk) * kD;
+    TR.k[0] = *reinterpret_cast<const u32x4*>(row + 16 * u);
+    TR.k[1] = *reinterpret_cast<const u32x4*>(row + 16 * u + 8);
+    TR.k[2] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u);
+    TR.k[3] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u + 8);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) TR.k[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int jv = 16 * q4 + (tid >> 4);
+    TR.v[q4] = jv < t_real_hint
+                   ? *reinterpret_cast<const u32x4*>(
+                         vn + (((size_t)b * T + jv) * p.Hkv + hk) * kD + (tid & 15) * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+__device__ __forceinline__ void load_tree_rope(TreeRaw& TR, const float* rope, int pos_j, int tid) {
+  const f32x4* cs = reinterpret_cast<const f32x4*>(rope + (size_t)pos_j * kD + 2 * 16 * (tid & 3));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) TR.cs[i] = cs[i];
+}
+__device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, int t_real,
+                                                int tid) {
+  const int j = tid >> 2, u = tid & 3;
+  u32x4 c[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (j < t_real) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x4 t4 = TR.cs[4 * h2 + w];
+        float y1a, y2a, y1b, y2b;
+        rope_pair_exact(bf16_lo(TR.k[h2][w]), bf16_lo(TR.k[2 + h2][w]), t4[0], t4[1], y1a, y2a);
+        rope_pair_exact(bf16_hi(TR.k[h2][w]), bf16_hi(TR.k[2 + h2][w]), t4[2], t4[3], y1b, y2b);
+        c[h2][w] = (uint32_t)f32_to_bf16_rne(y1a) | ((uint32_t)f32_to_bf16_rne(y1b) << 16);
+        c[2 + h2][w] = (uint32_t)f32_to_bf16_rne(y2a) | ((uint32_t)f32_to_bf16_rne(y2b) << 16);
+      }
+    }
+  }
+  char* kr = stage + j * kKRow;
+  *reinterpret_cast<u32x4*>(kr + 16 * (2 * u)) = c[0];
+  *reinterpret_cast<u32x4*>(kr + 16 * (2 * u + 1)) = c[1];
+  *reinterpret_cast<u32x4*>(kr + 16 * (8 + 2 * u)) = c[2];
+  *reinterpret_cast<u32x4*>(kr + 16 * (9 + 2 * u)) = c[3];
+  char* vb = stage + kKBytes + (tid >> 4) * kVRow + (tid & 15) * 16;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int jv = 16 * q4 + (tid >> 4);
+    *reinterpret_cast<u32x4*>(vb + 16 * q4 * kVRow) =
+        jv < t_real ? TR.v[q4] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+#ifdef TA_TRACE
+__device__ unsigned long long ta_trace_buf[1 << 16][8];
+#endif
+
+__global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(VerifyParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  static_assert(2 * 66 * 64 * sizeof(float) <= 2 * kStageBytes, "merge area");
+  __shared__ int s_pages[kMaxSplitPages];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int qt = wv >> 1, th = wv & 1;
+  const int g = lane >> 5, r32 = lane & 31;
+  // Work item: (sequence, head) major, split minor - no load needed, so the
+  // first round trip can carry everything that does not depend on ctx_len.
+  const int bh = blockIdx.x / p.splits, sp = blockIdx.x % p.splits;
+  const int b = bh / p.H, h = bh % p.H;
+#ifdef TA_TRACE
+  const unsigned long long trace_t0 = wall_clock64();
+#endif
+  const int hk = h / (p.H / p.Hkv);
+  const int T = p.T;
+  const int q = 32 * qt + r32;
+  const int c0 = sp * p.chunk;
+
+  // ---- round trip 1: ctx_len, tree rows, q row, tree k/v rows, page ids.
+  const int ctx_raw = p.ctx_lens[b];
+  const int par = lane < T ? p.tree_parent[(size_t)b * T + lane] : kPadParent;
+  const int dep = lane < T ? p.tree_depth[(size_t)b * T + lane] : 0;
+  QRaw Qr;
+  if (q < T) {
+    load_q_raw(Qr, static_cast<const uint16_t*>(p.q) + (((size_t)b * T + q) * p.H + h) * kD, g);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Qr.x[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  TreeRaw TR;
+  if (sp == 0) load_tree_raw(TR, p, b, hk, T, tid);
+  const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks;
+  const int max_pages = min(p.chunk / kPage, p.max_blocks - (c0 >> 4));
+  const int blk_raw = tid < max_pages ? table_row[(c0 >> 4) + tid] : -1;
+
+  const int ctx = clampi(ctx_raw, 0, p.max_ctx);
+  const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
+  if (sp >= nsplit) return;  // uniform: the whole workgroup leaves
+  const int c1 = min(ctx, c0 + p.chunk);
+  const int npages = (c1 - c0 + kPage - 1) / kPage;
+  if (tid < npages) s_pages[tid] = (blk_raw >= 0 && blk_raw < p.num_blocks) ? blk_raw : -1;
+
+  // Tree structure, one lane per node (every wavefront computes it).
+  const bool real = lane < T && par != kPadParent;
+  const uint64_t real_mask = __ballot(real);
+  const int t_real = real_mask == ~0ull ? 64 : __builtin_ctzll(~real_mask);  // real prefix
+  const bool linked = lane < t_real && (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+  uint64_t anc = linked ? (1ull << lane) : 0ull;
+  int up = (linked && lane > 0) ? par : lane;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const uint64_t a_up = __shfl(anc, up);
+    const int up_up = __shfl(up, up);
+    anc |= a_up;
+    up = up_up;
+  }
+  const int nqt = t_real > 32 ? 2 : 1;
+  const bool active = qt < nqt;
+  const uint64_t anc_q = __shfl(anc, q);
+  const bool row_real = active && q < t_real;
+  const int pos_q = ctx + clampi(__shfl(dep, q), 0, T - 1);
+  const int pos_j = ctx + clampi(__shfl(dep, tid >> 2), 0, T - 1);
+
+  __syncthreads();  // s_pages visible
+  // ---- round trip 2: the first context tiles and the (cos, sin) rows.
+  Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv};
+  const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
+  // Tile j of the split travels through registers R[j % kDepth]: kDepth
+  // tiles are in flight from HBM while one is computed out of LDS.
+  TileRegs R[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u)
+    if (u < n_tiles) load_ctx_tile(R[u], G, c0 + kTile * u, c1, tid);
+  QRope Rq;
+  load_q_rope(Rq, p.rope + (size_t)pos_q * kD, g);
+  if (sp == 0) load_tree_rope(TR, p.rope, pos_j, tid);
+
+  u32x4 qf[8];
+  if (row_real) {
+    rotate_q(qf, Qr, Rq, p.scale * kLog2e);
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) qf[s2] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  WaveState st;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) st.o[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  char* stage0 = smem;
+  char* stage1 = smem + kStageBytes;
+
+  const LaneOffs L = lane_offsets(lane, th);
+  if (sp == 0) {
+    store_tree_tile(stage1, TR, t_real, tid);
+    __syncthreads();
+    if (active) compute_tile<kTreeTile>(st, qf, stage1, L, kTile, anc_q);
+  }
+  if (n_tiles > 0) {
+    store_tile(R[0], stage0, tid);
+    __syncthreads();
+#ifdef TA_TRACE
+    if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][4] = wall_clock64();
+#endif
+    if (kDepth < n_tiles) load_ctx_tile(R[0], G, c0 + kTile * kDepth, c1, tid);
+    // Every tile but the last is full: one straight-line path, no masking.
+    for (int k0 = 0; k0 < n_tiles - 1; k0 += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int t = k0 + u;
+        if (t < n_tiles - 1) {
+          const int nu = (u + 1) % kDepth;
+          char* cur = (t & 1) ? stage1 : stage0;
+          char* nxt = (t & 1) ? stage0 : stage1;
+          if (active) compute_tile<kFull>(st, qf, cur, L, kTile, 0ull);
+          store_tile(R[nu], nxt, tid);
+          __syncthreads();
+          if (t + 1 + kDepth < n_tiles)
+            load_ctx_tile(R[nu], G, c0 + kTile * (t + 1 + kDepth), c1, tid);
+        }
+      }
+    }
+    // The last tile may end mid-tile.
+    const int t = n_tiles - 1;
+    char* cur = (t & 1) ? stage1 : stage0;
+    const int n_valid = c1 - (c0 + kTile * t);
+    if (active) {
+      if (n_valid >= kTile)
+        compute_tile<kFull>(st, qf, cur, L, kTile, 0ull);
+      else
+        compute_tile<kPartial>(st, qf, cur, L, n_valid, 0ull);
+    }
+  }
+
+  // Merge the two token halves of each query tile (wavefront th=1 -> th=0).
+  __syncthreads();
+#ifdef TA_TRACE
+  if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][5] = wall_clock64();
+#endif
+  float* mb = reinterpret_cast<float*>(smem);  // [2][66][64]
+  if (active && th == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb[(qt * 66 + dt * 16 + r) * 64 + lane] = st.o[dt][r];
+    mb[(qt * 66 + 64) * 64 + lane] = st.m;
+    mb[(qt * 66 + 65) * 64 + lane] = st.l;
+  }
+  __syncthreads();
+  if (th == 0) {
+    if (active) {
+      const float m1 = mb[(qt * 66 + 64) * 64 + lane];
+      const float l1 = mb[(qt * 66 + 65) * 64 + lane];
+      const float M = fmaxf(st.m, m1);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      const float w0 = __builtin_amdgcn_exp2f(st.m - Mu);
+      const float w1 = __builtin_amdgcn_exp2f(m1 - Mu);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          st.o[dt][r] = st.o[dt][r] * w0 + mb[(qt * 66 + dt * 16 + r) * 64 + lane] * w1;
+      st.l = st.l * w0 + l1 * w1;
+      st.m = M;
+      st.l += __shfl_xor(st.l, 32);
+    }
+    if (nsplit == 1) {
+      if (q < T) {
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + (((size_t)b * T + q) * p.H + h) * kD;
+        const float inv = (row_real && st.l > 0.f) ? 1.0f / st.l : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const f32x4 v4 = {st.o[dt][4 * rb] * inv, st.o[dt][4 * rb + 1] * inv,
+                              st.o[dt][4 * rb + 2] * inv, st.o[dt][4 * rb + 3] * inv};
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * rb + 4 * g) =
+                __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
+          }
+      }
+    } else if (row_real) {
+      const size_t row = ((size_t)bh * p.splits + sp) * T + q;
+      float* orow = p.ws_o + row * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * rb + 4 * g) =
+              f32x4{st.o[dt][4 * rb], st.o[dt][4 * rb + 1], st.o[dt][4 * rb + 2],
+                    st.o[dt][4 * rb + 3]};
+      if (g == 0) p.ws_ml[row] = float2{st.m, st.l};
+    }
+  }
+#ifdef TA_TRACE
+  if (tid == 0 && blockIdx.x < (1u << 16)) {
+    ta_trace_buf[blockIdx.x][0] = trace_t0;
+    ta_trace_buf[blockIdx.x][1] = wall_clock64();
+    ta_trace_buf[blockIdx.x][2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+    ta_trace_buf[blockIdx.x][3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+  }
+#endif
+}
+
+// Merge the (m, l, O) partials of every (sequence, head) whose context took
+// more than one split, and write its `out` rows (padding rows as zeros).  A
+// separate launch: the kernel boundary makes every split's partials visible,
+// where a device-wide fence inside the verify kernel would write back and
+// invalidate the L2 of its XCD once per workgroup.
+__global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh % p.H;
+  const int T = p.T;
+  const int ctx = clampi(p.ctx_lens[b], 0, p.max_ctx);
+  const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
+  if (nsplit == 1) return;
+  const int par = lane < T ? p.tree_parent[(size_t)b * T + lane] : kPadParent;
+  const uint64_t real_mask = __ballot(lane < T && par != kPadParent);
+  const int t_real = real_mask == ~0ull ? 64 : __builtin_ctzll(~real_mask);
+  const int cq = tid >> 2, part = tid & 3;
+  if (cq >= T) return;
+  uint16_t* orow =
+      static_cast<uint16_t*>(p.out) + (((size_t)b * T + cq) * p.H + h) * kD + 32 * part;
+  f32x8 acc[4] = {f32x8{}, f32x8{}, f32x8{}, f32x8{}};
+  float L = 0.f;
+  if (cq < t_real) {
+    const size_t row0 = (size_t)bh * p.splits * T + cq;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[row0 + (size_t)s * T].x);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    for (int s = 0; s < nsplit; ++s) {
+      const size_t row = row0 + (size_t)s * T;
+      const float2 ml = p.ws_ml[row];
+      const float w = __builtin_amdgcn_exp2f(ml.x - Mu);
+      L += w * ml.y;
+      const f32x8* src = reinterpret_cast<const f32x8*>(p.ws_o + row * kD + 32 * part);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += w * src[c];
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<u32x4*>(orow + 8 * c) =
+        __builtin_bit_cast(u32x4, __builtin_convertvector(acc[c] * inv, bf16x8));
+}
+
+}  // namespace
+
+#ifdef TA_TRACE
+extern "C" int ta_trace_fetch(void* host, size_t bytes) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(ta_trace_buf), bytes);
+}
+#endif
 
 hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream) {
-  (void)p;
-  (void)stream;
-  return hipErrorNotSupported;
+  const long long grid = (long long)p.B * p.H * p.splits;
+  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_mfma_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace ta

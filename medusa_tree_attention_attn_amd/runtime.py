@@ -24,7 +24,8 @@ class TreeVerifier:
     def __init__(self, *, batch: int, t_max: int, num_heads: int, num_kv_heads: int,
                  head_dim: int, max_blocks_per_seq: int, num_blocks: int, max_ctx_len: int,
                  dtype: torch.dtype = torch.bfloat16, device="cuda", rope_base: float = ROPE_BASE,
-                 scale: float = 0.0, flags: int = 0, rope_max_pos: Optional[int] = None):
+                 scale: float = 0.0, flags: int = 0, rope_max_pos: Optional[int] = None,
+                 split_tokens: int = 0):
         _lib.load()
         self.device = torch.device(device)
         self.dtype = dtype
@@ -38,8 +39,9 @@ class TreeVerifier:
             head_dim=head_dim, max_blocks_per_seq=max_blocks_per_seq, num_blocks=num_blocks,
             max_ctx_len=max_ctx_len, dtype=TA_BF16 if dtype == torch.bfloat16 else TA_F32,
             rope_table=self.rope, rope_max_pos=self.rope_max_pos, scale=scale, stream=stream,
-            flags=flags)
+            flags=flags, split_tokens=split_tokens)
         nbytes = tree_attn_workspace_size(self.desc)
+        self.workspace_bytes_needed = nbytes
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         self.desc.workspace = self.workspace.data_ptr()
         self.desc.workspace_bytes = self.workspace.numel()

@@ -19,14 +19,15 @@ def dev(wl, device="cuda"):
         cand_tokens=i32(wl.cand_tokens))
 
 
-def verifier(wl, flags=0, device="cuda", max_ctx_len=None):
+def verifier(wl, flags=0, device="cuda", max_ctx_len=None, split_tokens=0):
     from medusa_tree_attention_attn_amd import TreeVerifier
     s = wl.spec
     return TreeVerifier(batch=s.batch, t_max=s.t_max, num_heads=s.heads,
                         num_kv_heads=s.kv_heads, head_dim=s.head_dim,
                         max_blocks_per_seq=wl.max_blocks, num_blocks=wl.num_blocks,
                         max_ctx_len=wl.max_ctx_len if max_ctx_len is None else max_ctx_len,
-                        dtype=wl.torch_dtype, device=device, flags=flags)
+                        dtype=wl.torch_dtype, device=device, flags=flags,
+                        split_tokens=split_tokens)
 
 
 def sub_problem(wl, seqs):

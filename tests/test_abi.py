@@ -122,10 +122,10 @@ def test_accept_null_and_dims(lib, which):
 
 
 def test_workspace_requirement(lib):
-    desc = _desc()
+    # long contexts over few (sequence, head) pairs: the plan splits them
+    desc = _desc(max_ctx_len=4000, max_blocks_per_seq=260, rope_max_pos=4064)
     need = lib.tree_attn_workspace_size(ctypes.byref(desc))
-    if need == 0:
-        pytest.skip("this descriptor takes a kernel without workspace")
+    assert need > 0
     desc.workspace = 0x5000
     desc.workspace_bytes = need - 1
     assert _verify_rc(lib, desc) == -8
@@ -134,12 +134,32 @@ def test_workspace_requirement(lib):
     assert _verify_rc(lib, desc) == -8
 
 
+def test_misaligned_tensor_pointers(lib):
+    desc = _desc()
+    need = lib.tree_attn_workspace_size(ctypes.byref(desc))
+    desc.workspace = 0x100000
+    desc.workspace_bytes = need
+    for which in (0, 1, 2, 3, 8):                 # q, k_new, v_new, kv_pages, out
+        args = [0x2000 + 0x100 * i for i in range(9)]
+        args[which] += 8
+        assert lib.tree_attn_verify(ctypes.byref(desc), *args) == -12
+    args = [0x2000 + 0x100 * i for i in range(7)]
+    args[0] += 2                                  # k_new
+    assert lib.kv_commit_path(ctypes.byref(desc), *args) == -12
+    desc2 = _desc(rope_table=0x1004)
+    desc2.workspace, desc2.workspace_bytes = 0x100000, need
+    assert _verify_rc(lib, desc2) == -12
+
+
 def test_workspace_size_grows_with_context(lib):
     a = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=200)))
     b = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=4000, max_blocks_per_seq=260,
                                                         rope_max_pos=4064)))
     assert b >= a
-    simple = lib.tree_attn_workspace_size(ctypes.byref(_desc(flags=ta.TA_FLAG_SIMPLE_KERNEL)))
+    simple = lib.tree_attn_workspace_size(ctypes.byref(_desc(flags=ta.TA_FLAG_SIMPLE_KERNEL,
+                                                               max_ctx_len=4000,
+                                                               max_blocks_per_seq=260,
+                                                               rope_max_pos=4064)))
     assert simple == 0
     f32 = lib.tree_attn_workspace_size(ctypes.byref(_desc(dtype=ta.TA_F32)))
     assert f32 == 0

@@ -32,9 +32,9 @@ ATOL = 1e-2
 RTOL_OUT_ROUNDING = 2.0 ** -8
 
 
-def _verify_gpu(wl, flags=0, max_ctx_len=None):
+def _verify_gpu(wl, flags=0, max_ctx_len=None, split_tokens=0):
     d = dev(wl)
-    tv = verifier(wl, flags=flags, max_ctx_len=max_ctx_len)
+    tv = verifier(wl, flags=flags, max_ctx_len=max_ctx_len, split_tokens=split_tokens)
     out = tv.verify(d["q"], d["k_new"], d["v_new"], d["kv_pages"], d["block_table"],
                     d["ctx_lens"], d["tree_parent"], d["tree_depth"])
     torch.cuda.synchronize()
@@ -86,6 +86,34 @@ def test_verify_full(name, seed, kw, kernel):
     got = _verify_gpu(wl, flags)
     ref = oracle_verify_rows(wl, range(wl.spec.batch))
     _check_rows(got, ref, wl, list(range(wl.spec.batch)))
+
+
+@pytest.mark.parametrize("split_tokens", [64, 192, 512, 4096])
+def test_verify_split_sizes(split_tokens):
+    """One, a few and many split-KV work items per (sequence, head): the
+    partials and the fused last-arriving merge must agree with the oracle."""
+    wl = make_workload("vicuna7b_b16", 15, batch=4, heads=4, ctx_range=(1, 2000))
+    print(f"verify split_tokens={split_tokens}", flush=True)
+    got = _verify_gpu(wl, split_tokens=split_tokens)
+    ref = oracle_verify_rows(wl, range(4))
+    _check_rows(got, ref, wl, list(range(4)))
+
+
+def test_verify_repeated_calls_reuse_workspace():
+    """The arrival counters reset themselves: repeated calls on one workspace
+    give identical results."""
+    wl = make_workload("vicuna7b_b16", 16, batch=3, heads=4, ctx_range=(700, 1900))
+    d = dev(wl)
+    tv = verifier(wl, split_tokens=256)
+    outs = []
+    for _ in range(3):
+        o = tv.verify(d["q"], d["k_new"], d["v_new"], d["kv_pages"], d["block_table"],
+                      d["ctx_lens"], d["tree_parent"], d["tree_depth"])
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref = oracle_verify_rows(wl, range(3))
+    _check_rows(outs[0].float().cpu().numpy(), ref, wl, [0, 1, 2])
 
 
 def test_verify_chain_depth_63():
