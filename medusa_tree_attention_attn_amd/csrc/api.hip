@@ -89,6 +89,11 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   p.chunk = plan.chunk;
   p.splits = plan.splits;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 0;
+  p.n_cu = n_cu;
   if (plan.mfma) {
     char* ws = static_cast<char*>(d->workspace);
     p.ws_ml = reinterpret_cast<float2*>(ws + plan.off_ml);

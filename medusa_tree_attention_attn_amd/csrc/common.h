@@ -30,6 +30,7 @@ struct VerifyParams {
   int max_blocks, num_blocks, max_ctx, rope_max_pos;
   int chunk;               // context tokens per split work item
   int splits;              // max splits per (b, h) = ceil(max_ctx / chunk)
+  int n_cu;                // compute units of the device (work-item ordering)
   float scale;
 };
 

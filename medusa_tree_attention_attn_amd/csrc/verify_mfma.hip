@@ -339,6 +339,41 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
   }
 }
 
+#ifndef TA_ITEM_ORDER
+#define TA_ITEM_ORDER 0
+#endif
+#if TA_ITEM_ORDER
+// Launch slot -> (sequence, head), one split per pair, ranked by context
+// length.  When there are between one and two items per CU, slots 0..n_cu-1
+// take the longest items and slots n_cu.. take the shortest first, so the
+// two workgroups that share a CU hold about the average amount of work
+// (assuming the second round of slots lands on the CUs in the order of the
+// first).  Every lane of the wavefront takes part (lane = sequence).
+__device__ __forceinline__ bool paired_item(const VerifyParams& p, int slot, int lane, int& b,
+                                            int& h, int& sp) {
+  const int N = p.B * p.H;
+  if (p.B > 64 || p.splits != 1 || p.n_cu <= 0) {
+    b = (slot / p.splits) / p.H;
+    h = (slot / p.splits) % p.H;
+    sp = slot % p.splits;
+    return true;
+  }
+  sp = 0;
+  int r = slot;
+  if (N > p.n_cu && N < 2 * p.n_cu && slot >= p.n_cu) r = N - 1 - (slot - p.n_cu);
+  const int ctx_l = lane < p.B ? p.ctx_lens[lane] : -1;
+  int rank = 0;
+  for (int j = 0; j < p.B; ++j) {
+    const int cj = __shfl(ctx_l, j);
+    rank += (cj > ctx_l) || (cj == ctx_l && j < lane);
+  }
+  const int j = r / p.H;
+  h = r % p.H;
+  b = __builtin_ctzll(__ballot(lane < p.B && rank == j));
+  return r < N;
+}
+#endif
+
 #ifdef TA_TRACE
 __device__ unsigned long long ta_trace_buf[1 << 16][8];
 #endif
@@ -353,8 +388,14 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int g = lane >> 5, r32 = lane & 31;
   // Work item: (sequence, head) major, split minor - no load needed, so the
   // first round trip can carry everything that does not depend on ctx_len.
+#if TA_ITEM_ORDER
+  int b, h, sp;
+  if (!paired_item(p, blockIdx.x, lane, b, h, sp)) return;
+  const int bh = b * p.H + h;
+#else
   const int bh = blockIdx.x / p.splits, sp = blockIdx.x % p.splits;
   const int b = bh / p.H, h = bh % p.H;
+#endif
 #ifdef TA_TRACE
   const unsigned long long trace_t0 = wall_clock64();
 #endif
@@ -547,6 +588,8 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
     ta_trace_buf[blockIdx.x][1] = wall_clock64();
     ta_trace_buf[blockIdx.x][2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);
     ta_trace_buf[blockIdx.x][3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);
+    ta_trace_buf[blockIdx.x][6] = (unsigned long long)b;
+    ta_trace_buf[blockIdx.x][7] = (unsigned long long)h;
   }
 #endif
 }
