@@ -2,7 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = tree_attn_verify -> tree_accept_greedy -> kv_commit_path over one
+One step = tree_attn_verify -> tree_accept_commit (greedy acceptance and the
+KV commit of the accepted path in one launch; --separate-accept-commit runs
+tree_accept_greedy -> kv_commit_path instead) over one
 batch of the synthetic workload (default: batch 16, 32 heads, head_dim 128,
 bf16, contexts uniform in [256, 2048], trees of 64 nodes of depth <= 4,
 acceptance probability 0.3).  W untimed steps, then exactly K timed steps
@@ -52,6 +54,58 @@ def counted_traffic(workload: str):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+VERIFY_SOURCES = [
+    "medusa_tree_attention_attn_amd/csrc/verify_mfma.hip",
+    "medusa_tree_attention_attn_amd/csrc/common.h",
+    "medusa_tree_attention_attn_amd/csrc/plan.h",
+    "medusa_tree_attention_attn_amd/csrc/launch.h",
+]
+
+
+def write_traffic_record(fetch_csv: str, write_csv: str, workload: str, seed: int):
+    """Turn two rocprofv3 counter runs of this script (`--pmc FETCH_SIZE`,
+    then `--pmc WRITE_SIZE`, both with --calibrate-copy, csv output) into the
+    traffic record: per-dispatch means of the verify kernel, each scaled by
+    what the same counter reads for the 512 MiB device copies."""
+    import csv
+    import hashlib
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        verify = [float(r["Counter_Value"]) for r in rows
+                  if "verify_mfma_kernel(" in r["Kernel_Name"]]
+        copies = sorted(float(r["Counter_Value"]) for r in rows
+                        if "copyBuffer" in r["Kernel_Name"])
+        if not verify or len(copies) < 5:
+            raise SystemExit(f"{path}: no verify dispatches or no calibration copies")
+        return sum(verify) / len(verify), len(verify), sum(copies[-5:]) / 5
+
+    copy_kb = (512 << 20) / 1024
+    f_kb, nf, f_copy = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_kb, nw, w_copy = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = copy_kb / f_copy, copy_kb / w_copy
+    h = hashlib.sha256()
+    for f in VERIFY_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    rec = {
+        "kernel": "verify_mfma_kernel",
+        "workload": f"{workload} seed {seed}",
+        "sources": VERIFY_SOURCES,
+        "sources_sha256": h.hexdigest(),
+        "dispatches": [nf, nw],
+        "fetch_size_kb_per_dispatch": round(f_kb, 1),
+        "write_size_kb_per_dispatch": round(w_kb, 1),
+        "copy_calibration": {"bytes": float(512 << 20), "fetch_size_kb": round(f_copy, 1),
+                             "write_size_kb": round(w_copy, 1), "fetch_scale": round(f_scale, 4),
+                             "write_scale": round(w_scale, 4)},
+        "traffic_bytes_per_launch": int(round((f_kb * f_scale + w_kb * w_scale) * 1024)),
+    }
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 POOL_BYTES_TARGET = 1 << 30
 
 
@@ -166,9 +220,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-accept-commit", action="store_true",
+                    help="acceptance and commit as two launches instead of the fused one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 512 MiB device copies (for counter scaling)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the verify kernel's traffic record from two rocprofv3 "
+                         "counter-collection CSVs of this script, then exit (no GPU used)")
     args = ap.parse_args()
+    if args.traffic_record:
+        write_traffic_record(*args.traffic_record, args.workload, args.seed)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the tree-verify step shards by sequence or head with no exchange; "
@@ -210,11 +272,17 @@ def main():
         st = sets[k % copies]
         tv.verify(st["q"], st["k"], st["v"], st["pool"], table, ctx, par, dep, out=st["out"])
 
-    def step(k):
+    def accept_commit(k):
         st = sets[k % copies]
+        if args.separate_accept_commit:
+            tv.accept(amax, cand, par, L, P)
+            tv.commit(st["k"], st["v"], L, P, st["pool"], table, ctx)
+        else:
+            tv.accept_commit(amax, cand, par, st["k"], st["v"], st["pool"], table, ctx, L, P)
+
+    def step(k):
         verify(k)
-        tv.accept(amax, cand, par, L, P)
-        tv.commit(st["k"], st["v"], L, P, st["pool"], table, ctx)
+        accept_commit(k)
 
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -255,6 +323,12 @@ def main():
     vb.record()
     torch.cuda.synchronize()
     v_avg = va.elapsed_time(vb) / nv
+    va.record()
+    for k in range(nv):
+        accept_commit(k)
+    vb.record()
+    torch.cuda.synchronize()
+    ac_avg = va.elapsed_time(vb) / nv
     # restore the outputs of the step loop's last step for the parity check
     step(args.warmup + args.steps - 1)
     torch.cuda.synchronize()
@@ -315,6 +389,9 @@ def main():
             "avg_launch_us": round(v_avg * 1e3, 2),
         },
         "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "per_call_us": {"verify": round(v_avg * 1e3, 2),
+                        ("accept, commit" if args.separate_accept_commit else "accept_commit"):
+                            round(ac_avg * 1e3, 2)},
         "parity": {k: chk[k] for k in ("accept_bit_exact", "commit_bit_exact",
                                        "attn_max_abs_err")},
         "cpu_baseline": cpu,

@@ -171,6 +171,19 @@ int kv_commit_path(const tree_attn_desc* desc, const void* k_new, const void* v_
                    void* kv_pages, const int32_t* block_table,
                    const int32_t* ctx_lens);
 
+/* Greedy acceptance followed by the KV commit of the accepted path, in one
+ * launch (LMDeploy #1231 evaluate_posterior; mlc-llm #2319 KV-cache update).
+ * Writes accept_len and accept_path exactly as tree_accept_greedy does and
+ * kv_pages exactly as kv_commit_path would from those outputs; the checks and
+ * error codes are those of kv_commit_path plus a null test of the three
+ * acceptance inputs.  accept_len/accept_path are outputs here.  It saves one
+ * launch and one dependent memory round trip per step. */
+int tree_accept_commit(const tree_attn_desc* desc, const int32_t* node_argmax,
+                       const int32_t* cand_tokens, const int32_t* tree_parent,
+                       int32_t* accept_len, int32_t* accept_path, const void* k_new,
+                       const void* v_new, void* kv_pages, const int32_t* block_table,
+                       const int32_t* ctx_lens);
+
 /* Bytes of workspace tree_attn_verify needs for this descriptor (0 if the
  * descriptor is invalid).  Pure host computation. */
 size_t tree_attn_workspace_size(const tree_attn_desc* desc);

@@ -32,7 +32,7 @@ STATUS = {
     -10: "TA_ERR_CAPACITY", -11: "TA_ERR_LAUNCH", -12: "TA_ERR_ALIGNMENT",
 }
 EXPORTED = (
-    "tree_attn_verify", "tree_accept_greedy", "kv_commit_path",
+    "tree_attn_verify", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
     "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_rope_table",
     "tree_attn_strerror",
 )
@@ -85,6 +85,7 @@ def load() -> ctypes.CDLL:
         "tree_attn_verify": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "tree_accept_greedy": (ctypes.c_int, [D, P, P, P, P, P]),
         "kv_commit_path": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
+        "tree_accept_commit": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
         "tree_attn_workspace_size": (ctypes.c_size_t, [D]),
         "tree_attn_workspace_init": (ctypes.c_int, [D]),
         "tree_attn_rope_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_float,
@@ -206,6 +207,26 @@ def kv_commit_path(desc, k_new, v_new, accept_len, accept_path, kv_pages, block_
                                _ptr(accept_path), _ptr(kv_pages), _ptr(block_table),
                                _ptr(ctx_lens))
     _check(rc, "kv_commit_path")
+
+
+def tree_accept_commit(desc, node_argmax, cand_tokens, tree_parent, accept_len, accept_path,
+                       k_new, v_new, kv_pages, block_table, ctx_lens):
+    B, T, Hkv, d = desc.batch, desc.t_max, desc.num_kv_heads, desc.head_dim
+    dt = _dtype_of(desc)
+    for t, shp, name in ((node_argmax, (B, T), "node_argmax"), (cand_tokens, (B, T), "cand_tokens"),
+                         (tree_parent, (B, T), "tree_parent"), (accept_len, (B,), "accept_len"),
+                         (accept_path, (B, T), "accept_path")):
+        _expect(t, shp, torch.int32, name)
+    _expect(k_new, (B, T, Hkv, d), dt, "k_new")
+    _expect(v_new, (B, T, Hkv, d), dt, "v_new")
+    _expect(kv_pages, (desc.num_blocks, 2, Hkv, 16, d), dt, "kv_pages")
+    _expect(block_table, (B, desc.max_blocks_per_seq), torch.int32, "block_table")
+    _expect(ctx_lens, (B,), torch.int32, "ctx_lens")
+    rc = load().tree_accept_commit(ctypes.byref(desc), _ptr(node_argmax), _ptr(cand_tokens),
+                                   _ptr(tree_parent), _ptr(accept_len), _ptr(accept_path),
+                                   _ptr(k_new), _ptr(v_new), _ptr(kv_pages), _ptr(block_table),
+                                   _ptr(ctx_lens))
+    _check(rc, "tree_accept_commit")
 
 
 def tree_attn_workspace_size(desc) -> int:

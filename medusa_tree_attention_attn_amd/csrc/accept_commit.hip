@@ -15,13 +15,18 @@ namespace {
 //   accepted = every node on the root path is ok:  (anc_i & ~M) == 0
 //   end      = argmax over accepted nodes of (depth, -index)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ node_argmax,
-                                                    const int32_t* __restrict__ cand_tokens,
-                                                    const int32_t* __restrict__ tree_parent,
-                                                    int32_t* __restrict__ accept_len,
-                                                    int32_t* __restrict__ accept_path, int T) {
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
+struct Acceptance {
+  int len;          // accepted nodes, root included
+  uint64_t path;    // bit k set iff node k is on the accepted path
+  int depth;        // this lane's depth in the tree (meaningful on linked lanes)
+  bool in_tree;     // lane < T
+};
+
+// Called by one full wavefront; lane i evaluates node i of sequence b.
+__device__ __forceinline__ Acceptance accept_wave(const int32_t* __restrict__ node_argmax,
+                                                  const int32_t* __restrict__ cand_tokens,
+                                                  const int32_t* __restrict__ tree_parent, int b,
+                                                  int T, int i) {
   const bool in_tree = i < T;
   const size_t row = (size_t)b * T;
   const int par = in_tree ? tree_parent[row + i] : kPadParent;
@@ -46,12 +51,27 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ 
   for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
   const int end = 63 - (key & 63);       // key >= 0: the root is always accepted
   const uint64_t anc_end = __shfl(anc, end);
-  const int len = __popcll(anc_end);
-  if (in_tree) {
-    if ((anc_end >> i) & 1ull) accept_path[row + depth] = i;
-    if (i >= len) accept_path[row + i] = -1;
+  return Acceptance{(int)__popcll(anc_end), anc_end, depth, in_tree};
+}
+
+__device__ __forceinline__ void write_acceptance(const Acceptance& a, int32_t* accept_len,
+                                                 int32_t* accept_path, int b, int T, int i) {
+  const size_t row = (size_t)b * T;
+  if (a.in_tree) {
+    if ((a.path >> i) & 1ull) accept_path[row + a.depth] = i;
+    if (i >= a.len) accept_path[row + i] = -1;
   }
-  if (i == 0) accept_len[b] = len;
+  if (i == 0) accept_len[b] = a.len;
+}
+
+__global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ node_argmax,
+                                                    const int32_t* __restrict__ cand_tokens,
+                                                    const int32_t* __restrict__ tree_parent,
+                                                    int32_t* __restrict__ accept_len,
+                                                    int32_t* __restrict__ accept_path, int T) {
+  const int b = blockIdx.x, i = threadIdx.x;
+  const Acceptance a = accept_wave(node_argmax, cand_tokens, tree_parent, b, T, i);
+  write_acceptance(a, accept_len, accept_path, b, T, i);
 }
 
 // ---------------------------------------------------------------------------
@@ -94,13 +114,9 @@ __device__ __forceinline__ void store8(float* p, const float (&y)[8]) {
   reinterpret_cast<f32x4*>(p)[1] = f32x4{y[4], y[5], y[6], y[7]};
 }
 
+// Path slot i of sequence b holds node n: write its K/V rows at ctx_len + i.
 template <typename S>
-__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int len = p.accept_len[b];
-  if (i >= len || len > p.T) return;
-  const int n = p.accept_path[(size_t)b * p.T + i];
-  if (n < 0 || n >= p.T) return;
+__device__ __forceinline__ void commit_row(const CommitParams& p, int b, int i, int n) {
   const int pos = clampi(p.ctx_lens[b], 0, p.max_ctx) + i;
   const int lb = pos / kPage;
   if (lb >= p.max_blocks || pos >= p.rope_max_pos) return;
@@ -140,6 +156,42 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   }
 }
 
+template <typename S>
+__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int len = p.accept_len[b];
+  if (i >= len || len > p.T) return;
+  const int n = p.accept_path[(size_t)b * p.T + i];
+  if (n < 0 || n >= p.T) return;
+  commit_row<S>(p, b, i, n);
+}
+
+// Acceptance and commit in one launch: one workgroup per (path slot i,
+// sequence b).  Its first wavefront evaluates the sequence's tree (every
+// workgroup of the sequence gets the same answer); the workgroup of slot 0
+// publishes accept_len/accept_path, and each workgroup whose slot is on the
+// accepted path writes that row.  Same results as accept_kernel followed by
+// commit_kernel.
+template <typename S>
+__global__ __launch_bounds__(256) void accept_commit_kernel(CommitParams p,
+                                                            const int32_t* __restrict__ node_argmax,
+                                                            const int32_t* __restrict__ cand_tokens,
+                                                            const int32_t* __restrict__ tree_parent,
+                                                            int32_t* __restrict__ accept_len,
+                                                            int32_t* __restrict__ accept_path) {
+  __shared__ int s_node;
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  if (tid < 64) {
+    const Acceptance a = accept_wave(node_argmax, cand_tokens, tree_parent, b, p.T, tid);
+    if (i == 0) write_acceptance(a, accept_len, accept_path, b, p.T, tid);
+    const uint64_t at_i = __ballot(a.in_tree && ((a.path >> tid) & 1ull) && a.depth == i);
+    if (tid == 0) s_node = at_i ? __builtin_ctzll(at_i) : -1;
+  }
+  __syncthreads();
+  const int n = s_node;
+  if (n >= 0) commit_row<S>(p, b, i, n);
+}
+
 // (cos, sin) of pos * base^(-2k/d): angle in fp64, one rounding to fp32.
 __global__ void rope_table_kernel(int head_dim, double base, int max_pos, float* table) {
   const int half = head_dim / 2;
@@ -176,6 +228,20 @@ hipError_t launch_commit(const CommitParams& p, int dtype, hipStream_t stream) {
     hipLaunchKernelGGL(commit_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(commit_kernel<float>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_commit(const CommitParams& p, const int32_t* node_argmax,
+                                const int32_t* cand_tokens, const int32_t* tree_parent,
+                                int32_t* accept_len, int32_t* accept_path, int dtype,
+                                hipStream_t stream) {
+  dim3 grid(p.T, p.B);
+  if (dtype == TA_BF16)
+    hipLaunchKernelGGL(accept_commit_kernel<uint16_t>, grid, dim3(256), 0, stream, p, node_argmax,
+                       cand_tokens, tree_parent, accept_len, accept_path);
+  else
+    hipLaunchKernelGGL(accept_commit_kernel<float>, grid, dim3(256), 0, stream, p, node_argmax,
+                       cand_tokens, tree_parent, accept_len, accept_path);
   return hipGetLastError();
 }
 

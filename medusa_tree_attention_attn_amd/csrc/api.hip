@@ -116,9 +116,10 @@ int tree_accept_greedy(const tree_attn_desc* d, const int32_t* node_argmax,
                                  static_cast<hipStream_t>(d->stream)));
 }
 
-int kv_commit_path(const tree_attn_desc* d, const void* k_new, const void* v_new,
-                   const int32_t* accept_len, const int32_t* accept_path, void* kv_pages,
-                   const int32_t* block_table, const int32_t* ctx_lens) {
+namespace {
+int commit_params(const tree_attn_desc* d, const void* k_new, const void* v_new,
+                  const int32_t* accept_len, const int32_t* accept_path, void* kv_pages,
+                  const int32_t* block_table, const int32_t* ctx_lens, CommitParams& p) {
   const int rc = check_common(d);
   if (rc != TA_OK) return rc;
   if (!k_new || !v_new || !accept_len || !accept_path || !kv_pages || !block_table ||
@@ -127,7 +128,7 @@ int kv_commit_path(const tree_attn_desc* d, const void* k_new, const void* v_new
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_pages) ||
       !aligned16(d->rope_cos_sin))
     return TA_ERR_ALIGNMENT;
-  CommitParams p{};
+  p = CommitParams{};
   p.k_new = k_new;
   p.v_new = v_new;
   p.accept_len = accept_len;
@@ -144,7 +145,33 @@ int kv_commit_path(const tree_attn_desc* d, const void* k_new, const void* v_new
   p.num_blocks = d->num_blocks;
   p.max_ctx = d->max_ctx_len;
   p.rope_max_pos = d->rope_max_pos;
+  return TA_OK;
+}
+}  // namespace
+
+int kv_commit_path(const tree_attn_desc* d, const void* k_new, const void* v_new,
+                   const int32_t* accept_len, const int32_t* accept_path, void* kv_pages,
+                   const int32_t* block_table, const int32_t* ctx_lens) {
+  CommitParams p;
+  const int rc = commit_params(d, k_new, v_new, accept_len, accept_path, kv_pages, block_table,
+                               ctx_lens, p);
+  if (rc != TA_OK) return rc;
   return status_of(launch_commit(p, d->dtype, static_cast<hipStream_t>(d->stream)));
+}
+
+int tree_accept_commit(const tree_attn_desc* d, const int32_t* node_argmax,
+                       const int32_t* cand_tokens, const int32_t* tree_parent,
+                       int32_t* accept_len, int32_t* accept_path, const void* k_new,
+                       const void* v_new, void* kv_pages, const int32_t* block_table,
+                       const int32_t* ctx_lens) {
+  if (!node_argmax || !cand_tokens || !tree_parent) return TA_ERR_NULL_POINTER;
+  CommitParams p;
+  const int rc = commit_params(d, k_new, v_new, accept_len, accept_path, kv_pages, block_table,
+                               ctx_lens, p);
+  if (rc != TA_OK) return rc;
+  return status_of(launch_accept_commit(p, node_argmax, cand_tokens, tree_parent, accept_len,
+                                        accept_path, d->dtype,
+                                        static_cast<hipStream_t>(d->stream)));
 }
 
 int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* table,

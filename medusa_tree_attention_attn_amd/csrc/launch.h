@@ -33,6 +33,13 @@ struct CommitParams {
 };
 hipError_t launch_commit(const CommitParams& p, int dtype, hipStream_t stream);
 
+// Greedy acceptance and KV commit in one launch (same results as
+// launch_accept followed by launch_commit on its outputs).
+hipError_t launch_accept_commit(const CommitParams& p, const int32_t* node_argmax,
+                                const int32_t* cand_tokens, const int32_t* tree_parent,
+                                int32_t* accept_len, int32_t* accept_path, int dtype,
+                                hipStream_t stream);
+
 hipError_t launch_rope_table(int head_dim, float base, int max_pos, float* table,
                              hipStream_t stream);
 

@@ -46,6 +46,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kTile = 64;                       // tokens per LDS tile (four pages)
@@ -320,8 +322,10 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
         float y1a, y2a, y1b, y2b;
         rope_pair_exact(bf16_lo(TR.k[h2][w]), bf16_lo(TR.k[2 + h2][w]), t4[0], t4[1], y1a, y2a);
         rope_pair_exact(bf16_hi(TR.k[h2][w]), bf16_hi(TR.k[2 + h2][w]), t4[2], t4[3], y1b, y2b);
-        c[h2][w] = (uint32_t)f32_to_bf16_rne(y1a) | ((uint32_t)f32_to_bf16_rne(y1b) << 16);
-        c[2 + h2][w] = (uint32_t)f32_to_bf16_rne(y2a) | ((uint32_t)f32_to_bf16_rne(y2b) << 16);
+        // v_cvt_pk_bf16_f32 rounds to nearest even, as the commit's integer
+        // rounding does, for every finite value.
+        c[h2][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y1a, y1b}, bf16x2));
+        c[2 + h2][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y2a, y2b}, bf16x2));
       }
     }
   }
@@ -339,17 +343,17 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
   }
 }
 
-#ifndef TA_ITEM_ORDER
-#define TA_ITEM_ORDER 0
-#endif
-#if TA_ITEM_ORDER
-// Launch slot -> (sequence, head), one split per pair, ranked by context
-// length.  When there are between one and two items per CU, slots 0..n_cu-1
-// take the longest items and slots n_cu.. take the shortest first, so the
-// two workgroups that share a CU hold about the average amount of work
-// (assuming the second round of slots lands on the CUs in the order of the
-// first).  Every lane of the wavefront takes part (lane = sequence).
-__device__ __forceinline__ bool paired_item(const VerifyParams& p, int slot, int lane, int& b,
+// Launch slot -> (sequence, head, split).  With one split per pair and at
+// most 64 sequences, pairs are ranked by context length (longest first, one
+// sequence's heads together).  When there are between one and two pairs per
+// CU, slots 0..n_cu-1 take the longest pairs and slot n_cu + i takes the i-th
+// shortest: the dispatcher fills every CU with slots i and i + n_cu, so each
+// CU then holds one long and one short pair and about the average number of
+// tiles.  With more pairs than that, longest-first order lets the dispatcher
+// hand the short tail to whichever CU frees up first.  Otherwise (splits, or
+// more than 64 sequences) the order is (sequence, head) major, split minor.
+// Every lane of the wavefront takes part (lane = sequence).
+__device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int lane, int& b,
                                             int& h, int& sp) {
   const int N = p.B * p.H;
   if (p.B > 64 || p.splits != 1 || p.n_cu <= 0) {
@@ -360,7 +364,7 @@ __device__ __forceinline__ bool paired_item(const VerifyParams& p, int slot, int
   }
   sp = 0;
   int r = slot;
-  if (N > p.n_cu && N < 2 * p.n_cu && slot >= p.n_cu) r = N - 1 - (slot - p.n_cu);
+  if (N > p.n_cu && N <= 2 * p.n_cu && slot >= p.n_cu) r = N - 1 - (slot - p.n_cu);
   const int ctx_l = lane < p.B ? p.ctx_lens[lane] : -1;
   int rank = 0;
   for (int j = 0; j < p.B; ++j) {
@@ -372,10 +376,10 @@ __device__ __forceinline__ bool paired_item(const VerifyParams& p, int slot, int
   b = __builtin_ctzll(__ballot(lane < p.B && rank == j));
   return r < N;
 }
-#endif
 
 #ifdef TA_TRACE
-__device__ unsigned long long ta_trace_buf[1 << 16][8];
+__device__ unsigned long long ta_trace_buf[1 << 16][12];
+#define TA_STAMP(i) do { if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][i] = wall_clock64(); } while (0)
 #endif
 
 __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(VerifyParams p) {
@@ -386,16 +390,9 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qt = wv >> 1, th = wv & 1;
   const int g = lane >> 5, r32 = lane & 31;
-  // Work item: (sequence, head) major, split minor - no load needed, so the
-  // first round trip can carry everything that does not depend on ctx_len.
-#if TA_ITEM_ORDER
   int b, h, sp;
-  if (!paired_item(p, blockIdx.x, lane, b, h, sp)) return;
+  if (!launch_item(p, blockIdx.x, lane, b, h, sp)) return;
   const int bh = b * p.H + h;
-#else
-  const int bh = blockIdx.x / p.splits, sp = blockIdx.x % p.splits;
-  const int b = bh / p.H, h = bh % p.H;
-#endif
 #ifdef TA_TRACE
   const unsigned long long trace_t0 = wall_clock64();
 #endif
@@ -450,6 +447,9 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int pos_j = ctx + clampi(__shfl(dep, tid >> 2), 0, T - 1);
 
   __syncthreads();  // s_pages visible
+#ifdef TA_TRACE
+  TA_STAMP(8);
+#endif
   // ---- round trip 2: the first context tiles and the (cos, sin) rows.
   Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv};
   const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
@@ -481,18 +481,27 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   char* stage1 = smem + kStageBytes;
 
   const LaneOffs L = lane_offsets(lane, th);
-  if (sp == 0) {
-    store_tree_tile(stage1, TR, t_real, tid);
-    __syncthreads();
-    if (active) compute_tile<kTreeTile>(st, qf, stage1, L, kTile, anc_q);
-  }
-  if (n_tiles > 0) {
-    store_tile(R[0], stage0, tid);
-    __syncthreads();
 #ifdef TA_TRACE
-    if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][4] = wall_clock64();
+  TA_STAMP(9);
 #endif
-    if (kDepth < n_tiles) load_ctx_tile(R[0], G, c0 + kTile * kDepth, c1, tid);
+  // Tree tile -> stage 1 and context tile 0 -> stage 0 behind one barrier;
+  // the next context tile's loads then overlap the tree tile's compute.
+  if (sp == 0) store_tree_tile(stage1, TR, t_real, tid);
+  if (n_tiles > 0) store_tile(R[0], stage0, tid);
+  __syncthreads();
+  if (kDepth < n_tiles) load_ctx_tile(R[0], G, c0 + kTile * kDepth, c1, tid);
+#ifdef TA_TRACE
+  TA_STAMP(10);
+#endif
+  if (sp == 0) {
+    if (active) compute_tile<kTreeTile>(st, qf, stage1, L, kTile, anc_q);
+    __syncthreads();  // stage 1 is refilled by the loop's first store
+  }
+#ifdef TA_TRACE
+  TA_STAMP(11);
+  TA_STAMP(4);
+#endif
+  if (n_tiles > 0) {
     // Every tile but the last is full: one straight-line path, no masking.
     for (int k0 = 0; k0 < n_tiles - 1; k0 += kDepth) {
 #pragma unroll

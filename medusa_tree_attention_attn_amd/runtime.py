@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_greedy,
+from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_commit,
+                   tree_accept_greedy,
                    tree_attn_rope_table, tree_attn_verify, tree_attn_workspace_init,
                    tree_attn_workspace_size)
 
@@ -74,3 +75,16 @@ class TreeVerifier:
         self._sync_stream()
         kv_commit_path(self.desc, k_new, v_new, accept_len, accept_path, kv_pages, block_table,
                        ctx_lens)
+
+    def accept_commit(self, node_argmax, cand_tokens, tree_parent, k_new, v_new, kv_pages,
+                      block_table, ctx_lens, accept_len=None, accept_path=None):
+        """accept() then commit() of its result, in one library launch."""
+        self._sync_stream()
+        B, T = self.desc.batch, self.desc.t_max
+        if accept_len is None:
+            accept_len = torch.empty((B,), dtype=torch.int32, device=self.device)
+        if accept_path is None:
+            accept_path = torch.empty((B, T), dtype=torch.int32, device=self.device)
+        tree_accept_commit(self.desc, node_argmax, cand_tokens, tree_parent, accept_len,
+                           accept_path, k_new, v_new, kv_pages, block_table, ctx_lens)
+        return accept_len, accept_path

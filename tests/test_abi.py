@@ -97,6 +97,7 @@ def test_null_descriptor(lib):
     assert lib.tree_attn_verify(None, *([None] * 9)) == -1
     assert lib.tree_accept_greedy(None, *([None] * 5)) == -1
     assert lib.kv_commit_path(None, *([None] * 7)) == -1
+    assert lib.tree_accept_commit(None, *([0x3000] * 10)) == -1
     assert lib.tree_attn_workspace_size(None) == 0
     assert lib.tree_attn_workspace_init(None) == -1
 
@@ -119,6 +120,19 @@ def test_accept_null_and_dims(lib, which):
     good = [0x3000 + 0x100 * i for i in range(5)]
     assert lib.tree_accept_greedy(ctypes.byref(_desc(t_max=65)), *good) == -4
     assert lib.tree_accept_greedy(ctypes.byref(_desc(batch=0)), *good) == -2
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_accept_commit_null_and_checks(lib, which):
+    args = [0x3000 + 0x100 * i for i in range(10)]
+    args[which] = None
+    assert lib.tree_accept_commit(ctypes.byref(_desc()), *args) == -1
+    good = [0x3000 + 0x100 * i for i in range(10)]
+    assert lib.tree_accept_commit(ctypes.byref(_desc(t_max=65)), *good) == -4
+    assert lib.tree_accept_commit(ctypes.byref(_desc(batch=0)), *good) == -2
+    bad = list(good)
+    bad[5] += 2                                   # k_new misaligned
+    assert lib.tree_accept_commit(ctypes.byref(_desc()), *bad) == -12
 
 
 def test_workspace_requirement(lib):

@@ -304,6 +304,49 @@ def test_commit_stress_full_size():
     assert torch.equal(pool_bits(got), pool_bits(ref))
 
 
+@pytest.mark.parametrize("name,seed,kw", [
+    ("tiny", 0, {}), ("tiny", 2, dict(ctx_range=(0, 31))),
+    ("vicuna7b_bs1", 1, {}), ("vicuna7b_b16", 0, {}), ("vicuna13b_b8", 1, {}),
+    ("stress_b64", 4, dict(batch=12, heads=4, ctx_range=(0, 200))),
+])
+def test_accept_commit_fused_bit_exact(name, seed, kw):
+    """The one-launch acceptance + commit against the oracle's accept_greedy
+    then commit: accept_len, accept_path and every byte of the pool."""
+    wl = make_workload(name, seed, **kw)
+    d = dev(wl)
+    tv = verifier(wl)
+    L, P = tv.accept_commit(d["node_argmax"], d["cand_tokens"], d["tree_parent"], d["k_new"],
+                            d["v_new"], d["kv_pages"], d["block_table"], d["ctx_lens"])
+    torch.cuda.synchronize()
+    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+    assert np.array_equal(L.cpu().numpy(), Lr) and np.array_equal(P.cpu().numpy(), Pr)
+    rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
+    ref = oracle.commit(wl.k_new, wl.v_new, Lr, Pr, wl.kv_pages, wl.block_table, wl.ctx_lens,
+                        rope)
+    diff = (pool_bits(d["kv_pages"].cpu()) != pool_bits(ref)).nonzero()
+    assert diff.numel() == 0, f"{diff.shape[0]} differing elements"
+
+
+def test_accept_commit_fused_long_paths():
+    """Every candidate matches: the accepted path reaches the deepest node."""
+    wl = make_workload("vicuna13b_b8", 2, heads=4, ctx_range=(1, 300))
+    import dataclasses
+    wl = dataclasses.replace(wl, node_argmax=np.full_like(wl.node_argmax, 9),
+                             cand_tokens=np.full_like(wl.cand_tokens, 9))
+    d = dev(wl)
+    tv = verifier(wl)
+    L, P = tv.accept_commit(d["node_argmax"], d["cand_tokens"], d["tree_parent"], d["k_new"],
+                            d["v_new"], d["kv_pages"], d["block_table"], d["ctx_lens"])
+    torch.cuda.synchronize()
+    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+    assert np.array_equal(L.cpu().numpy(), Lr) and np.array_equal(P.cpu().numpy(), Pr)
+    assert Lr.min() == wl.tree_depth.max(axis=1).min() + 1
+    rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
+    ref = oracle.commit(wl.k_new, wl.v_new, Lr, Pr, wl.kv_pages, wl.block_table, wl.ctx_lens,
+                        rope)
+    assert torch.equal(pool_bits(d["kv_pages"].cpu()), pool_bits(ref))
+
+
 # ------------------------------------------------------------------- rope --
 
 @pytest.mark.parametrize("d", [64, 128])
