@@ -56,6 +56,7 @@ def counted_traffic(workload: str):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 VERIFY_SOURCES = [
     "medusa_tree_attention_attn_amd/csrc/verify_mfma.hip",
+    "medusa_tree_attention_attn_amd/csrc/mfma_tile.h",
     "medusa_tree_attention_attn_amd/csrc/common.h",
     "medusa_tree_attention_attn_amd/csrc/plan.h",
     "medusa_tree_attention_attn_amd/csrc/launch.h",

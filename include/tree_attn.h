@@ -75,8 +75,14 @@ enum ta_dtype { TA_BF16 = 0, TA_F32 = 1 };
 
 /* desc->flags bits */
 enum ta_flags {
-  TA_FLAG_SIMPLE_KERNEL = 1   /* verify with the plain one-wavefront-per-node  */
-                              /* kernel even where the MFMA kernel applies     */
+  TA_FLAG_SIMPLE_KERNEL = 1,  /* verify with the plain one-wavefront-per-node  */
+                              /* kernel even where the MFMA kernels apply      */
+  TA_FLAG_GRID_KERNEL = 2,    /* MFMA verify: one workgroup per work item      */
+  TA_FLAG_PERSISTENT_KERNEL = 4 /* MFMA verify: one resident workgroup per CU   */
+                              /* taking work items from a counter.  Without    */
+                              /* either flag the library takes the persistent  */
+                              /* kernel when there are at least 4 work items   */
+                              /* per CU, else the grid kernel.                 */
 };
 
 enum ta_status {
@@ -133,9 +139,13 @@ typedef struct tree_attn_desc {
  *                  . keys) . values, accumulated in fp32 and rounded to
  *                  dtype (round to nearest even).
  * Padding rows of out are written as zeros.  kv_pages is only read.
- * Needs desc->workspace of tree_attn_workspace_size(desc) bytes (its
- * contents need no initialisation; it holds split-KV partials between the
- * two kernels of one call).  Errors: every TA_ERR_* code. */
+ * Needs desc->workspace of tree_attn_workspace_size(desc) bytes.  For the
+ * MFMA kernels (bf16, head_dim 128) its first 256 bytes hold the persistent
+ * kernel's work counters: zero-fill the workspace once with
+ * tree_attn_workspace_init before its first verify; every verify leaves
+ * them at zero again.  The rest holds split-KV partials between the kernels
+ * of one call and needs no initialisation.  The current device must be the
+ * one desc->stream belongs to.  Errors: every TA_ERR_* code. */
 int tree_attn_verify(const tree_attn_desc* desc, const void* q, const void* k_new,
                      const void* v_new, const void* kv_pages,
                      const int32_t* block_table, const int32_t* ctx_lens,
@@ -189,8 +199,9 @@ int tree_accept_commit(const tree_attn_desc* desc, const int32_t* node_argmax,
 size_t tree_attn_workspace_size(const tree_attn_desc* desc);
 
 /* Zero-fills desc->workspace (desc->workspace_bytes bytes) on desc->stream
- * with a fill kernel.  Optional: tree_attn_verify does not need a cleared
- * workspace. */
+ * with a fill kernel.  Required once before a workspace's first
+ * tree_attn_verify when tree_attn_workspace_size is non-zero (the persistent
+ * kernel's work counters must start at zero). */
 int tree_attn_workspace_init(const tree_attn_desc* desc);
 
 /* Fills table[pos][k][0..1] = (cos, sin)(pos * base^(-2k/head_dim)) for

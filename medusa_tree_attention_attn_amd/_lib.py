@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtree_att
 TA_BF16 = 0
 TA_F32 = 1
 TA_FLAG_SIMPLE_KERNEL = 1
+TA_FLAG_GRID_KERNEL = 2
+TA_FLAG_PERSISTENT_KERNEL = 4
 
 STATUS = {
     0: "TA_OK", -1: "TA_ERR_NULL_POINTER", -2: "TA_ERR_BAD_DIMS", -3: "TA_ERR_DTYPE",

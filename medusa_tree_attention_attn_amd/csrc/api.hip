@@ -96,9 +96,21 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   p.n_cu = n_cu;
   if (plan.mfma) {
     char* ws = static_cast<char*>(d->workspace);
-    p.ws_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
-    p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
-    return status_of(launch_verify_mfma(p, stream));
+    if (plan.splits > 1) {
+      p.ws_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
+      p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
+    }
+    hipError_t e;
+    const long long items = (long long)p.B * p.H * p.splits;
+    if (use_stream_kernel(*d, items, n_cu)) {
+      if (n_cu <= 0) return TA_ERR_LAUNCH;
+      p.ws_ctr = reinterpret_cast<uint32_t*>(ws + plan.off_ctr);
+      e = launch_verify_stream(p, stream);
+    } else {
+      e = launch_verify_mfma(p, stream);
+    }
+    if (e == hipSuccess && plan.splits > 1) e = launch_split_combine(p, stream);
+    return status_of(e);
   }
   return status_of(launch_verify_simple(p, d->dtype, stream));
 }

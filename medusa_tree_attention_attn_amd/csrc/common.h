@@ -26,6 +26,7 @@ struct VerifyParams {
   const float* rope;       // [rope_max_pos][d/2][2]
   float* ws_o;             // split partials: O  [B][H][splits][T][d]
   float2* ws_ml;           // split partials: (m, l) [B][H][splits][T]
+  uint32_t* ws_ctr;        // work counters of the persistent kernel (2 words, kept zero between launches)
   int B, T, H, Hkv, D;
   int max_blocks, num_blocks, max_ctx, rope_max_pos;
   int chunk;               // context tokens per split work item

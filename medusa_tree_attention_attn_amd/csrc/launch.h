@@ -12,9 +12,13 @@ namespace ta {
 // bf16 or fp32.  Plain and slow; no workspace.
 hipError_t launch_verify_simple(const VerifyParams& p, int dtype, hipStream_t stream);
 
-// MFMA split-KV kernel for bf16, head_dim 128, followed (when a context can
-// take more than one split) by the kernel that merges the split partials.
+// MFMA kernels for bf16, head_dim 128: one workgroup per work item, or the
+// persistent kernel (one workgroup per CU, work items taken from the
+// counters at p.ws_ctr).  When a context can take more than one split, the
+// split partials are merged by launch_split_combine afterwards.
 hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream);
+hipError_t launch_verify_stream(const VerifyParams& p, hipStream_t stream);
+hipError_t launch_split_combine(const VerifyParams& p, hipStream_t stream);
 
 hipError_t launch_accept(const int32_t* node_argmax, const int32_t* cand_tokens,
                          const int32_t* tree_parent, int32_t* accept_len,

@@ -8,7 +8,7 @@
 
 namespace ta {
 
-// Split-KV sizing of the MFMA kernel.  A (sequence, head) whose context fits
+// Split-KV sizing of the MFMA kernels.  A (sequence, head) whose context fits
 // in one split is one work item and writes `out` directly; longer contexts
 // are cut into splits of `chunk` tokens (a multiple of the 64-token tile)
 // whose partials a second kernel merges.  Each work item pays a prologue
@@ -22,9 +22,11 @@ constexpr int kTileTokens = 64;
 constexpr int kMaxSplitTokens = 4096;   // the kernel keeps a split's page ids in LDS
 
 struct Plan {
-  bool mfma;         // MFMA kernel (bf16, head_dim 128) or the plain kernel
+  bool mfma;         // MFMA kernels (bf16, head_dim 128) or the plain kernel
+  bool stream;       // persistent MFMA kernel may run (workspace has its counters)
   int chunk;         // tokens per split
   int splits;        // max splits per (sequence, head)
+  size_t off_ctr;    // uint32 [2] work counters of the persistent kernel
   size_t off_ml;     // float2 [B][H][splits][T] (running max, running sum)
   size_t off_o;      // float [B][H][splits][T][128] un-normalised partial O
   size_t bytes;      // total workspace
@@ -32,9 +34,21 @@ struct Plan {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Persistent kernel or one workgroup per work item.  The persistent kernel
+// balances the CUs dynamically but streams a little slower per CU (one
+// pipeline per CU instead of two co-resident workgroups); it wins once each
+// CU has several work items to balance.
+constexpr int kStreamItemsPerCu = 4;
+inline bool use_stream_kernel(const tree_attn_desc& d, long long items, int n_cu) {
+  if (d.flags & TA_FLAG_GRID_KERNEL) return false;
+  if (d.flags & TA_FLAG_PERSISTENT_KERNEL) return true;
+  return n_cu > 0 && items >= (long long)kStreamItemsPerCu * n_cu;
+}
+
 inline Plan make_plan(const tree_attn_desc& d) {
   Plan p{};
   p.mfma = d.dtype == TA_BF16 && d.head_dim == 128 && !(d.flags & TA_FLAG_SIMPLE_KERNEL);
+  p.stream = p.mfma;
   const int max_ctx = d.max_ctx_len > 0 ? d.max_ctx_len : 1;
   int chunk;
   if (d.split_tokens > 0) {
@@ -50,12 +64,20 @@ inline Plan make_plan(const tree_attn_desc& d) {
   if (chunk > kMaxSplitTokens) chunk = kMaxSplitTokens;
   p.chunk = chunk;
   p.splits = (max_ctx + chunk - 1) / chunk;
-  if (!p.mfma || p.splits == 1) return p;  // no partials: no workspace
-  const size_t bh = (size_t)d.batch * d.num_heads;
-  const size_t rows = bh * (size_t)p.splits * d.t_max;
-  p.off_ml = 0;
-  p.off_o = p.off_ml + align256(rows * 8);
-  p.bytes = p.off_o + align256(rows * (size_t)d.head_dim * sizeof(float));
+  if (!p.mfma) return p;
+  size_t off = 0;
+  if (p.stream) {
+    p.off_ctr = 0;
+    off = 256;
+  }
+  if (p.splits > 1) {
+    const size_t bh = (size_t)d.batch * d.num_heads;
+    const size_t rows = bh * (size_t)p.splits * d.t_max;
+    p.off_ml = off;
+    p.off_o = p.off_ml + align256(rows * 8);
+    off = p.off_o + align256(rows * (size_t)d.head_dim * sizeof(float));
+  }
+  p.bytes = off;
   return p;
 }
 

@@ -33,36 +33,17 @@
 // trips: everything that does not depend on ctx_len (tree rows, q row, tree
 // k/v rows, page ids), then the (cos, sin) rows and the first context tile.
 #include "launch.h"
+#include "mfma_tile.h"
 #include "plan.h"
 
 namespace ta {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kD = 128;
 constexpr int kTile = 64;                       // tokens per LDS tile (four pages)
 constexpr int kThreads = 256;
-// LDS tiles are row-major (one token per row) with padded rows: 16 lanes that
-// read one 16-byte chunk from 16 consecutive K rows, or one 64-bit transpose
-// read from 4 consecutive V rows x 32 bytes, land in distinct banks, and every
-// access is a lane-constant address plus an immediate offset.
-constexpr int kKRow = 256 + 16;
-constexpr int kVRow = 256 + 32;
 constexpr int kKBytes = kTile * kKRow;
 constexpr int kVBytes = kTile * kVRow;
 constexpr int kStageBytes = kKBytes + kVBytes;
-constexpr float kLog2e = 1.44269504088896341f;
-constexpr float kSlack = 8.0f;                  // log2 units: p <= 2^8 before a rescale
 constexpr int kMaxSplitPages = kMaxSplitTokens / kPage;
 
 // Pipeline depth (context tiles in flight per workgroup) and the occupancy
@@ -74,27 +55,6 @@ constexpr int kMaxSplitPages = kMaxSplitTokens / kPage;
 #define TA_WG_PER_CU 2
 #endif
 constexpr int kDepth = TA_PREFETCH_TILES;
-
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
-
-__device__ __forceinline__ f32x16 mfma(const u32x4& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// gfx950 transpose read: within each group of 16 lanes, lane a points at four
-// consecutive 16-bit values E[a][0..3]; lane i receives E[4k + i/4][i%4] for
-// k = 0..3.  With lane a = 4k + r pointing at row (t0 + k), columns
-// d0 + 4r .. d0 + 4r + 3 of a row-major tile, lane i gets column d0 + i of
-// rows t0 .. t0+3: a column slice of V, as the PV operand needs it.
-__device__ __forceinline__ v4i16 ds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(p));
-}
 
 // One tile's worth of global data held by a thread between load and store:
 // row tid/16 (of page p), 16-byte chunk tid%16, of the K and of the V plane.
@@ -143,85 +103,6 @@ __device__ __forceinline__ void store_tile(const TileRegs& R, char* stage, int t
     *reinterpret_cast<u32x4*>(kb + 16 * p * kKRow) = R.k[p];
     *reinterpret_cast<u32x4*>(vb + 16 * p * kVRow) = R.v[p];
   }
-}
-
-struct WaveState {
-  f32x16 o[4];  // O^T, d tiles of 32: lane owns query column, rows = d
-  float m, l;   // running max (log2 units) and this lane half's running sum
-};
-
-// Lane-constant LDS offsets of wavefront (qt, th) inside a stage.
-struct LaneOffs {
-  int k;   // K operand: row 32*th + lane%32, chunk lane/32 (+32 bytes per k-step)
-  int v;   // V transpose read: see ds_read_tr
-  int base;
-  int g;
-};
-
-__device__ __forceinline__ LaneOffs lane_offsets(int lane, int th) {
-  LaneOffs L;
-  const int g = lane >> 5, r32 = lane & 31;
-  const int grp = lane >> 4, a = lane & 15;
-  L.base = 32 * th;
-  L.g = g;
-  L.k = (L.base + r32) * kKRow + g * 16;
-  L.v = kKBytes + (L.base + 4 * (grp >> 1) + (a >> 2)) * kVRow + (16 * (grp & 1) + 4 * (a & 3)) * 2;
-  return L;
-}
-
-enum TileMode { kFull = 0, kPartial = 1, kTreeTile = 2 };
-
-// One 64-token tile for wavefront (qt, th): tokens 32*th .. 32*th+31.
-template <int kMode>
-__device__ __forceinline__ void compute_tile(WaveState& st, const u32x4 (&qf)[8],
-                                             const char* stage, const LaneOffs& L, int n_valid,
-                                             uint64_t anc_q) {
-  f32x16 s = {};
-  const char* kp = stage + L.k;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    s = mfma(*reinterpret_cast<const u32x4*>(kp + 32 * ks), qf[ks], s);
-  if (kMode != kFull) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tt = L.base + 8 * (r >> 2) + 4 * L.g + (r & 3);
-      const bool ok = kMode == kTreeTile ? ((anc_q >> tt) & 1ull) != 0ull : tt < n_valid;
-      s[r] = ok ? s[r] : -INFINITY;
-    }
-  }
-  float tmax = s[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float m_new = (tmax > st.m + kSlack) ? tmax : st.m;
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-  f32x8 p0, p1;
-  float psum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    p0[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
-    p1[r] = __builtin_amdgcn_exp2f(s[r + 8] - m_use);
-    psum += p0[r] + p1[r];
-  }
-  st.l = st.l * alpha + psum;
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= alpha;
-  }
-  st.m = m_new;
-  const bf16x8 pk[2] = {__builtin_convertvector(p0, bf16x8), __builtin_convertvector(p1, bf16x8)};
-  const char* vp = stage + L.v;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const v4i16 lo = ds_read_tr(vp + (16 * ks) * kVRow + 64 * dt);
-      const v4i16 hi = ds_read_tr(vp + (16 * ks + 8) * kVRow + 64 * dt);
-      const v8i16 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ks],
-                                                          st.o[dt], 0, 0, 0);
-    }
 }
 
 // Q^T fragments of query row q for k-steps 0..7 (chunk 2*ks + g), rotated at
@@ -472,15 +353,12 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   }
 
   WaveState st;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) st.o[dt] = f32x16{};
-  st.m = -INFINITY;
-  st.l = 0.f;
+  reset(st);
 
   char* stage0 = smem;
   char* stage1 = smem + kStageBytes;
 
-  const LaneOffs L = lane_offsets(lane, th);
+  const LaneOffs L = lane_offsets(lane, th, kKBytes);
 #ifdef TA_TRACE
   TA_STAMP(9);
 #endif
@@ -536,60 +414,15 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
 #ifdef TA_TRACE
   if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][5] = wall_clock64();
 #endif
-  float* mb = reinterpret_cast<float*>(smem);  // [2][66][64]
-  if (active && th == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mb[(qt * 66 + dt * 16 + r) * 64 + lane] = st.o[dt][r];
-    mb[(qt * 66 + 64) * 64 + lane] = st.m;
-    mb[(qt * 66 + 65) * 64 + lane] = st.l;
-  }
+  float* mb = reinterpret_cast<float*>(smem) + qt * kParkFloats;  // [2][66][64]
+  if (active && th == 1) park_state(st, mb, lane);
   __syncthreads();
   if (th == 0) {
     if (active) {
-      const float m1 = mb[(qt * 66 + 64) * 64 + lane];
-      const float l1 = mb[(qt * 66 + 65) * 64 + lane];
-      const float M = fmaxf(st.m, m1);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float w0 = __builtin_amdgcn_exp2f(st.m - Mu);
-      const float w1 = __builtin_amdgcn_exp2f(m1 - Mu);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          st.o[dt][r] = st.o[dt][r] * w0 + mb[(qt * 66 + dt * 16 + r) * 64 + lane] * w1;
-      st.l = st.l * w0 + l1 * w1;
-      st.m = M;
+      merge_state(st, mb, mb[64 * 64 + lane], mb[65 * 64 + lane], lane);
       st.l += __shfl_xor(st.l, 32);
     }
-    if (nsplit == 1) {
-      if (q < T) {
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + (((size_t)b * T + q) * p.H + h) * kD;
-        const float inv = (row_real && st.l > 0.f) ? 1.0f / st.l : 0.f;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            const f32x4 v4 = {st.o[dt][4 * rb] * inv, st.o[dt][4 * rb + 1] * inv,
-                              st.o[dt][4 * rb + 2] * inv, st.o[dt][4 * rb + 3] * inv};
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * rb + 4 * g) =
-                __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
-          }
-      }
-    } else if (row_real) {
-      const size_t row = ((size_t)bh * p.splits + sp) * T + q;
-      float* orow = p.ws_o + row * kD;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * rb + 4 * g) =
-              f32x4{st.o[dt][4 * rb], st.o[dt][4 * rb + 1], st.o[dt][4 * rb + 2],
-                    st.o[dt][4 * rb + 3]};
-      if (g == 0) p.ws_ml[row] = float2{st.m, st.l};
-    }
+    write_result(st, p, b, h, bh, sp, nsplit, q, T, row_real, g);
   }
 #ifdef TA_TRACE
   if (tid == 0 && blockIdx.x < (1u << 16)) {
@@ -659,8 +492,10 @@ hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream) {
   const long long grid = (long long)p.B * p.H * p.splits;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(verify_mfma_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_split_combine(const VerifyParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -11,7 +11,10 @@ on sampled sequences (sub-problems holding only the pages those sequences
 reference), chosen to include the longest and shortest contexts and every tree
 size of the stress mix.  Edge cases: empty context, single-node trees,
 contexts that end mid-page, padded (ragged) trees, chains reaching depth 63,
-grouped-query heads.
+grouped-query heads.  The MFMA path has two kernels (one workgroup per work
+item, and a persistent one that takes work items from a counter); both are
+run on the edge cases, the persistent one also on consecutive calls that
+share its counters.
 """
 import numpy as np
 import pytest
@@ -76,25 +79,29 @@ FULL_CASES = [
 ]
 
 
+KERNEL_FLAGS = {"default": 0, "simple": 1, "grid": 2, "persistent": 4}
+
+
 @pytest.mark.parametrize("name,seed,kw", FULL_CASES,
                          ids=[f"{n}-s{s}-{i}" for i, (n, s, _) in enumerate(FULL_CASES)])
-@pytest.mark.parametrize("kernel", ["default", "simple"])
+@pytest.mark.parametrize("kernel", ["default", "persistent", "simple"])
 def test_verify_full(name, seed, kw, kernel):
     wl = make_workload(name, seed, **kw)
-    flags = 1 if kernel == "simple" else 0
+    flags = KERNEL_FLAGS[kernel]
     print(f"verify {name} seed={seed} {kw} kernel={kernel}", flush=True)
     got = _verify_gpu(wl, flags)
     ref = oracle_verify_rows(wl, range(wl.spec.batch))
     _check_rows(got, ref, wl, list(range(wl.spec.batch)))
 
 
+@pytest.mark.parametrize("kernel", ["grid", "persistent"])
 @pytest.mark.parametrize("split_tokens", [64, 192, 512, 4096])
-def test_verify_split_sizes(split_tokens):
+def test_verify_split_sizes(split_tokens, kernel):
     """One, a few and many split-KV work items per (sequence, head): the
-    partials and the fused last-arriving merge must agree with the oracle."""
+    partials and their merge must agree with the oracle."""
     wl = make_workload("vicuna7b_b16", 15, batch=4, heads=4, ctx_range=(1, 2000))
-    print(f"verify split_tokens={split_tokens}", flush=True)
-    got = _verify_gpu(wl, split_tokens=split_tokens)
+    print(f"verify split_tokens={split_tokens} kernel={kernel}", flush=True)
+    got = _verify_gpu(wl, flags=KERNEL_FLAGS[kernel], split_tokens=split_tokens)
     ref = oracle_verify_rows(wl, range(4))
     _check_rows(got, ref, wl, list(range(4)))
 
@@ -116,12 +123,50 @@ def test_verify_repeated_calls_reuse_workspace():
     _check_rows(outs[0].float().cpu().numpy(), ref, wl, [0, 1, 2])
 
 
-def test_verify_chain_depth_63():
+@pytest.mark.parametrize("kernel", ["grid", "persistent"])
+def test_verify_chain_depth_63(kernel):
     wl = make_workload("vicuna7b_bs1", 8, batch=2, heads=2, ctx_range=(17, 40),
                        tree_sizes=(64,), chain=True)
-    got = _verify_gpu(wl)
+    got = _verify_gpu(wl, flags=KERNEL_FLAGS[kernel])
     ref = oracle_verify_rows(wl, [0, 1])
     _check_rows(got, ref, wl, [0, 1])
+
+
+def test_persistent_kernel_counters_reset_between_calls():
+    """The persistent kernel takes work items from counters in the workspace
+    and its last workgroup zeroes them: consecutive calls on one workspace,
+    with different numbers of work items (so different grids), each match
+    the oracle, and a repeat of the first call is bit-identical to it."""
+    from medusa_tree_attention_attn_amd import TreeVerifier
+    big = make_workload("stress_b64", 21, batch=40, heads=32, ctx_range=(1, 900))
+    small = make_workload("stress_b64", 22, batch=3, heads=5, ctx_range=(0, 300))
+    s = big.spec
+    tv = TreeVerifier(batch=s.batch, t_max=s.t_max, num_heads=32, num_kv_heads=32,
+                      head_dim=128, max_blocks_per_seq=big.max_blocks,
+                      num_blocks=big.num_blocks, max_ctx_len=big.max_ctx_len,
+                      dtype=torch.bfloat16, flags=KERNEL_FLAGS["persistent"],
+                      split_tokens=4096)
+    tv_small = TreeVerifier(batch=3, t_max=s.t_max, num_heads=5, num_kv_heads=5,
+                            head_dim=128, max_blocks_per_seq=small.max_blocks,
+                            num_blocks=small.num_blocks, max_ctx_len=small.max_ctx_len,
+                            dtype=torch.bfloat16, flags=KERNEL_FLAGS["persistent"],
+                            split_tokens=4096)
+    # share one workspace between the two descriptors
+    assert tv_small.workspace_bytes_needed <= tv.workspace.numel()
+    tv_small.desc.workspace = tv.workspace.data_ptr()
+    tv_small.desc.workspace_bytes = tv.workspace.numel()
+    db, ds = dev(big), dev(small)
+    args = lambda d: (d["q"], d["k_new"], d["v_new"], d["kv_pages"], d["block_table"],
+                      d["ctx_lens"], d["tree_parent"], d["tree_depth"])
+    o1 = tv.verify(*args(db)).clone()
+    o2 = tv_small.verify(*args(ds)).clone()
+    o3 = tv.verify(*args(db)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3)
+    _check_rows(o2.float().cpu().numpy(), oracle_verify_rows(small, range(3)), small, [0, 1, 2])
+    seqs = [0, 17, 39]
+    ref = oracle_verify_rows(big, seqs)
+    _check_rows(o1.float().cpu().numpy()[seqs], ref, big, seqs)
 
 
 def _sample_seqs(wl, k):
@@ -149,7 +194,8 @@ def test_verify_sampled_full_size(name, seed, nseq, heads):
     _check_rows(got[seqs][:, :, heads], ref, wl, seqs)
 
 
-def test_verify_grouped_query_heads():
+@pytest.mark.parametrize("kernel", ["grid", "persistent"])
+def test_verify_grouped_query_heads(kernel):
     wl = make_workload("vicuna7b_b16", 9, batch=2, heads=8, ctx_range=(50, 400))
     # 8 query heads sharing 2 KV heads: keep every 4th KV head of the draw
     kn = wl.k_new[:, :, ::4].contiguous()
@@ -158,7 +204,7 @@ def test_verify_grouped_query_heads():
     import dataclasses
     spec = dataclasses.replace(wl.spec, kv_heads=2)
     wl = dataclasses.replace(wl, spec=spec, k_new=kn, v_new=vn, kv_pages=pool)
-    got = _verify_gpu(wl)
+    got = _verify_gpu(wl, flags=KERNEL_FLAGS[kernel])
     ref = oracle_verify_rows(wl, [0, 1])
     _check_rows(got, ref, wl, [0, 1])
 
