@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "verify_mfma_vicuna7b_b16_traffic.json")
 
 
-def counted_traffic(workload: str):
+def counted_traffic(workload: str, kernel: str):
     """HBM bytes per verify launch from the committed rocprofv3 counter runs
     (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), or None
     when the kernel sources changed since the counters were taken or the
@@ -47,7 +47,7 @@ def counted_traffic(workload: str):
         rec = json.load(open(TRAFFIC_RECORD))
     except (OSError, ValueError):
         return None
-    if not rec.get("workload", "").startswith(workload + " "):
+    if not rec.get("workload", "").startswith(workload + " ") or rec.get("kernel") != kernel:
         return None
     h = hashlib.sha256()
     for f in rec["sources"]:
@@ -266,8 +266,11 @@ def main():
                       head_dim=s.head_dim, max_blocks_per_seq=wl.max_blocks,
                       num_blocks=wl.num_blocks, max_ctx_len=wl.max_ctx_len,
                       dtype=wl.torch_dtype, split_tokens=args.split_tokens)
+    from medusa_tree_attention_attn_amd._lib import tree_attn_plan_info
+    kernel_name, n_splits, split_tokens = tree_attn_plan_info(tv.desc)
     log(f"{copies} rotating input copies ({copies * pool_bytes / 1e9:.2f} GB of KV pool), "
-        f"workspace {tv.workspace.numel() / 1e6:.1f} MB")
+        f"workspace {tv.workspace.numel() / 1e6:.1f} MB; {kernel_name}, {n_splits} split(s) "
+        f"of {split_tokens} tokens")
 
     def verify(k):
         st = sets[k % copies]
@@ -373,18 +376,19 @@ def main():
             "global_batch": s.batch,
             "tree_tokens_per_step": wl.tree_tokens,
             "mean_ctx": float(wl.ctx_lens.mean()),
-            "split_tokens": tv.desc.split_tokens or "auto",
+            "split_tokens": split_tokens,
+            "splits": n_splits,
             "rotating_copies": copies,
             "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "verify_mfma_kernel" + (" + combine_kernel" if tv.workspace_bytes_needed else ""),
+            "kernel": kernel_name + (" + combine_kernel" if n_splits > 1 else ""),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (counted_traffic(args.workload)
+            "traffic": (counted_traffic(args.workload, kernel_name)
                         if args.seed == 0 and args.split_tokens == 0 else None),
             "bytes_per_launch": nbytes["verify"],
             "avg_launch_us": round(v_avg * 1e3, 2),

@@ -198,6 +198,15 @@ int tree_accept_commit(const tree_attn_desc* desc, const int32_t* node_argmax,
  * descriptor is invalid).  Pure host computation. */
 size_t tree_attn_workspace_size(const tree_attn_desc* desc);
 
+/* Kernels tree_attn_verify launches for this descriptor on the current
+ * device: *kernel = TA_KERNEL_SIMPLE, TA_KERNEL_GRID or TA_KERNEL_PERSISTENT;
+ * *splits = context splits per (sequence, head) (a merge kernel follows when
+ * it is > 1); *split_tokens = context tokens per split.  Output pointers may
+ * be NULL.  Host-only query; errors as tree_attn_verify's descriptor checks. */
+enum ta_kernel { TA_KERNEL_SIMPLE = 0, TA_KERNEL_GRID = 1, TA_KERNEL_PERSISTENT = 2 };
+int tree_attn_plan_info(const tree_attn_desc* desc, int32_t* kernel, int32_t* splits,
+                        int32_t* split_tokens);
+
 /* Zero-fills desc->workspace (desc->workspace_bytes bytes) on desc->stream
  * with a fill kernel.  Required once before a workspace's first
  * tree_attn_verify when tree_attn_workspace_size is non-zero (the persistent

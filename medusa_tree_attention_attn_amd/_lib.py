@@ -35,7 +35,7 @@ STATUS = {
 }
 EXPORTED = (
     "tree_attn_verify", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
-    "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_rope_table",
+    "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_plan_info", "tree_attn_rope_table",
     "tree_attn_strerror",
 )
 
@@ -90,6 +90,7 @@ def load() -> ctypes.CDLL:
         "tree_accept_commit": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
         "tree_attn_workspace_size": (ctypes.c_size_t, [D]),
         "tree_attn_workspace_init": (ctypes.c_int, [D]),
+        "tree_attn_plan_info": (ctypes.c_int, [D, P, P, P]),
         "tree_attn_rope_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_float,
                                                 ctypes.c_int32, P, P]),
         "tree_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -229,6 +230,18 @@ def tree_accept_commit(desc, node_argmax, cand_tokens, tree_parent, accept_len, 
                                    _ptr(k_new), _ptr(v_new), _ptr(kv_pages), _ptr(block_table),
                                    _ptr(ctx_lens))
     _check(rc, "tree_accept_commit")
+
+
+KERNEL_NAMES = {0: "verify_simple_kernel", 1: "verify_mfma_kernel", 2: "verify_stream_kernel"}
+
+
+def tree_attn_plan_info(desc):
+    """(kernel name, splits, split_tokens) tree_attn_verify will use."""
+    k, sp, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = load().tree_attn_plan_info(ctypes.byref(desc), ctypes.byref(k), ctypes.byref(sp),
+                                    ctypes.byref(ch))
+    _check(rc, "tree_attn_plan_info")
+    return KERNEL_NAMES[k.value], sp.value, ch.value
 
 
 def tree_attn_workspace_size(desc) -> int:

@@ -31,6 +31,15 @@ int status_of(hipError_t e) { return e == hipSuccess ? TA_OK : TA_ERR_LAUNCH; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Compute units of the current device (0 when the query fails).
+int device_cu_count() {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n_cu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -38,6 +47,22 @@ extern "C" {
 size_t tree_attn_workspace_size(const tree_attn_desc* d) {
   if (check_common(d) != TA_OK) return 0;
   return make_plan(*d).bytes;
+}
+
+int tree_attn_plan_info(const tree_attn_desc* d, int32_t* kernel, int32_t* splits,
+                        int32_t* split_tokens) {
+  const int rc = check_common(d);
+  if (rc != TA_OK) return rc;
+  const Plan plan = make_plan(*d);
+  int k = TA_KERNEL_SIMPLE;
+  if (plan.mfma) {
+    const long long items = (long long)d->batch * d->num_heads * plan.splits;
+    k = use_stream_kernel(*d, items, device_cu_count()) ? TA_KERNEL_PERSISTENT : TA_KERNEL_GRID;
+  }
+  if (kernel) *kernel = k;
+  if (splits) *splits = plan.splits;
+  if (split_tokens) *split_tokens = plan.chunk;
+  return TA_OK;
 }
 
 int tree_attn_workspace_init(const tree_attn_desc* d) {
@@ -89,10 +114,7 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   p.chunk = plan.chunk;
   p.splits = plan.splits;
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    n_cu = 0;
+  const int n_cu = device_cu_count();
   p.n_cu = n_cu;
   if (plan.mfma) {
     char* ws = static_cast<char*>(d->workspace);

@@ -135,6 +135,25 @@ def test_accept_commit_null_and_checks(lib, which):
     assert lib.tree_accept_commit(ctypes.byref(_desc()), *bad) == -12
 
 
+def test_plan_info_follows_flags(lib):
+    """The kernel choice is a host-side rule: forced by the flags, else the
+    persistent kernel only with >= 4 work items per CU (no device here: 0 CUs,
+    so the grid kernel); splits come from the context bound."""
+    out = [ctypes.c_int32() for _ in range(3)]
+    refs = [ctypes.byref(x) for x in out]
+    assert lib.tree_attn_plan_info(ctypes.byref(_desc()), *refs) == 0
+    assert out[0].value == 1 and out[1].value == 1            # grid kernel, one split
+    assert lib.tree_attn_plan_info(ctypes.byref(_desc(flags=4)), *refs) == 0
+    assert out[0].value == 2                                  # persistent forced
+    assert lib.tree_attn_plan_info(ctypes.byref(_desc(flags=1)), *refs) == 0
+    assert out[0].value == 0                                  # plain kernel
+    desc = _desc(max_ctx_len=4000, max_blocks_per_seq=260, rope_max_pos=4064)
+    assert lib.tree_attn_plan_info(ctypes.byref(desc), *refs) == 0
+    assert out[1].value > 1 and out[1].value * out[2].value >= 4000
+    assert lib.tree_attn_plan_info(ctypes.byref(desc), None, None, None) == 0
+    assert lib.tree_attn_plan_info(None, *refs) == -1
+
+
 def test_workspace_requirement(lib):
     # long contexts over few (sequence, head) pairs: the plan splits them
     desc = _desc(max_ctx_len=4000, max_blocks_per_seq=260, rope_max_pos=4064)
