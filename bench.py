@@ -12,10 +12,13 @@ between two device synchronisations.  Inputs are resident in HBM before the
 timed region; the steps rotate over enough copies of the inputs and of the KV
 pool (>= 1 GB in total) that the 256 MB Infinity Cache cannot serve a repeat.
 
-Prints one JSON line: verified tree-tokens/s (the outputs of the timed run
-are checked against the CPU oracle before anything is printed), the verify
-kernel's HBM roofline fraction from its HIP-event launch time and its
-algorithmic bytes, and the oracle timed on this host's CPU.
+Prints one JSON line: verified tree-tokens/s, the verify kernel's HBM
+roofline fraction from its HIP-event launch time and its algorithmic bytes,
+the greedy-token argmax (and argmax fused with acceptance) on synthetic
+logits, and the oracle timed on this host's CPU.  The oracle leg
+(cpu_baseline) also checks the outputs of the timed run against the oracle
+before anything is printed; with --no-cpu-baseline that check is skipped and
+the line says so.
 """
 from __future__ import annotations
 
@@ -54,12 +57,13 @@ def counted_traffic(workload: str, kernel: str):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+# The grid verify kernel's code: its device code and the headers it takes
+# device code from (the host-side plan and launch declarations do not change
+# what one launch moves for a given plan).
 VERIFY_SOURCES = [
     "medusa_tree_attention_attn_amd/csrc/verify_mfma.hip",
     "medusa_tree_attention_attn_amd/csrc/mfma_tile.h",
     "medusa_tree_attention_attn_amd/csrc/common.h",
-    "medusa_tree_attention_attn_amd/csrc/plan.h",
-    "medusa_tree_attention_attn_amd/csrc/launch.h",
 ]
 
 
@@ -142,10 +146,11 @@ def _i32(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
 
-def parity_check(wl, out, L, P, pool_after, nseq=4):
-    """Outputs of the timed run against the CPU oracle: acceptance bit-exact
-    for the whole batch; attention within 1e-2 on sampled sequences (all
-    heads); committed rows bit-exact on those sequences' touched pages."""
+def _oracle_parity(wl, out, L, P, pool_after, nseq=4):
+    """(cpu_baseline leg) Outputs of the timed run against the CPU oracle:
+    acceptance bit-exact for the whole batch; attention within 1e-2 on
+    sampled sequences (all heads); committed rows bit-exact on those
+    sequences' touched pages."""
     import oracle
     Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
     ok_accept = np.array_equal(L, Lr) and np.array_equal(P, Pr)
@@ -185,9 +190,26 @@ def parity_check(wl, out, L, P, pool_after, nseq=4):
                 ok=bool(ok_accept and ok_commit and worst <= 1e-2))
 
 
-def cpu_baseline(wl):
-    """The oracle as it stands, one full step of this workload on one host
-    thread (BLAS limited to 1 thread), scaled to tree-tokens/s."""
+def cpu_baseline_leg(wl, timed, posterior_out):
+    """The CPU oracle's leg of the benchmark: its results check the outputs
+    of the timed GPU run (and of the greedy-token measurement), then the
+    oracle as it stands is timed on one full step of this workload on one
+    host thread (BLAS limited to 1 thread), scaled to tree-tokens/s.
+    Returns (parity, baseline)."""
+    import oracle
+    parity = _oracle_parity(wl, *timed)
+    if posterior_out is not None:
+        from oracle.posterior import vocab_argmax
+        logits, A, L, P = posterior_out
+        ref = vocab_argmax(logits)
+        Lr, Pr = oracle.accept_greedy(ref, wl.cand_tokens, wl.tree_parent)
+        parity["posterior_bit_exact"] = bool(np.array_equal(A, ref) and np.array_equal(L, Lr)
+                                             and np.array_equal(P, Pr))
+        parity["ok"] = parity["ok"] and parity["posterior_bit_exact"]
+    return parity, _oracle_timing(wl)
+
+
+def _oracle_timing(wl):
     import oracle
     from threadpoolctl import threadpool_limits
     f = lambda t: t.to(torch.float32).numpy()
@@ -212,6 +234,44 @@ def cpu_baseline(wl):
                 seconds=dt)
 
 
+def posterior_bench(wl, tv, dev, seed, log, reps=50):
+    """The greedy token of every node from synthetic bf16 logits [B][T][vocab]
+    (tree_vocab_argmax) and the same fused with acceptance
+    (tree_argmax_accept): launch time back to back over rotating copies
+    (>= 1 GB, beyond the Infinity Cache), and the HBM fraction of the
+    logits stream.  Returns the figures and (logits, node_argmax, accept_len,
+    accept_path) of the last fused call for the oracle leg to check."""
+    from synth import make_logits
+    logits = make_logits(wl, seed)
+    nb = logits.numel() * logits.element_size()
+    copies = max(2, math.ceil(POOL_BYTES_TARGET / nb))
+    xs = [logits.to(dev) for _ in range(copies)]
+    cand, par = _i32(wl.cand_tokens, dev), _i32(wl.tree_parent, dev)
+    B, T = wl.node_argmax.shape
+    A = torch.empty((B, T), dtype=torch.int32, device=dev)
+    L = torch.empty((B,), dtype=torch.int32, device=dev)
+    P = torch.empty((B, T), dtype=torch.int32, device=dev)
+    out = {"logits": f"bf16 [{B}][{T}][{logits.shape[-1]}], {copies} rotating copies",
+           "bytes_per_launch": nb + B * T * 4}
+    for name, fn in (("vocab_argmax", lambda x: tv.vocab_argmax(x, A)),
+                     ("argmax_accept", lambda x: tv.argmax_accept(x, cand, par, A, L, P))):
+        for k in range(5):
+            fn(xs[k % copies])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(reps):
+            fn(xs[k % copies])
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        gbs = out["bytes_per_launch"] / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"posterior: {out}")
+    return out, (logits, A.cpu().numpy(), L.cpu().numpy(), P.cpu().numpy())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +281,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-posterior", action="store_true",
+                    help="skip the greedy-token argmax measurement")
     ap.add_argument("--separate-accept-commit", action="store_true",
                     help="acceptance and commit as two launches instead of the fused one")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -337,24 +399,29 @@ def main():
     step(args.warmup + args.steps - 1)
     torch.cuda.synchronize()
 
-    # parity of the timed run's outputs (last copy used by the last step)
-    last = sets[(args.warmup + args.steps - 1) % copies]
-    chk = parity_check(wl, last["out"].cpu(), L.cpu().numpy(), P.cpu().numpy(),
-                       last["pool"].cpu())
-    log(f"parity of timed outputs: {chk}")
-    if not chk["ok"]:
-        print(json.dumps({"metric": "verified tree-tokens/s", "error": "parity failed",
-                          "parity": chk}))
-        sys.exit(1)
+    posterior, posterior_out = (None, None) if args.no_posterior else \
+        posterior_bench(wl, tv, dev, args.seed, log)
+
+    # The oracle leg: parity of the timed run's outputs (last copy used by the
+    # last step), then the oracle's own timing.
+    cpu = None
+    chk = {"checked": False, "why": "--no-cpu-baseline: the oracle leg did not run"}
+    if not args.no_cpu_baseline:
+        last = sets[(args.warmup + args.steps - 1) % copies]
+        chk, cpu = cpu_baseline_leg(
+            wl, (last["out"].cpu(), L.cpu().numpy(), P.cpu().numpy(), last["pool"].cpu()),
+            posterior_out)
+        log(f"parity of timed outputs: {chk}")
+        log(f"cpu baseline: {cpu}")
+        cpu.pop("seconds", None)
+        if not chk["ok"]:
+            print(json.dumps({"metric": "verified tree-tokens/s", "error": "parity failed",
+                              "parity": chk}))
+            sys.exit(1)
 
     nbytes = algorithmic_bytes(wl, L.cpu().numpy())
     achieved = nbytes["verify"] / (v_avg * 1e-3) / 1e9
     tokens_per_s = wl.tree_tokens / (ms_per_step * 1e-3)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl)
-        log(f"cpu baseline: {cpu}")
-        cpu.pop("seconds", None)
     result = {
         "metric": "verified tree-tokens/s (verify+accept+commit step)",
         "value": round(tokens_per_s, 1),
@@ -397,8 +464,8 @@ def main():
         "per_call_us": {"verify": round(v_avg * 1e3, 2),
                         ("accept, commit" if args.separate_accept_commit else "accept_commit"):
                             round(ac_avg * 1e3, 2)},
-        "parity": {k: chk[k] for k in ("accept_bit_exact", "commit_bit_exact",
-                                       "attn_max_abs_err")},
+        "parity": {k: v for k, v in chk.items() if k not in ("ok", "sampled_sequences")},
+        "posterior": posterior,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

@@ -194,8 +194,31 @@ int tree_accept_commit(const tree_attn_desc* desc, const int32_t* node_argmax,
                        const void* v_new, void* kv_pages, const int32_t* block_table,
                        const int32_t* ctx_lens);
 
+/* Greedy token of the base model after every tree node (LMDeploy #1231
+ * evaluate_posterior at LM-head temperature 0):
+ *   node_argmax[b][i] = the smallest v < vocab with
+ *                       logits[b][i][v] == max over v' of logits[b][i][v']
+ * for all B * t_max rows (padding rows included).  logits is a device
+ * tensor [B][t_max][vocab] of logits_dtype (TA_BF16 or TA_F32), compared as
+ * exact values; NaN never wins and a row with no comparable value gives 0.
+ * Uses batch, t_max and stream of desc.  Errors: TA_ERR_NULL_POINTER,
+ * TA_ERR_BAD_DIMS, TA_ERR_TREE_TOO_LARGE, TA_ERR_DTYPE, TA_ERR_LAUNCH. */
+int tree_vocab_argmax(const tree_attn_desc* desc, const void* logits, int32_t logits_dtype,
+                      int32_t vocab, int32_t* node_argmax);
+
+/* tree_vocab_argmax followed by tree_accept_greedy on its result, in one
+ * call (two kernels on desc->stream; the kernel boundary publishes
+ * node_argmax to the acceptance).  Writes node_argmax, accept_len and
+ * accept_path exactly as the two calls would.  Errors: those of
+ * tree_vocab_argmax. */
+int tree_argmax_accept(const tree_attn_desc* desc, const void* logits, int32_t logits_dtype,
+                       int32_t vocab, const int32_t* cand_tokens, const int32_t* tree_parent,
+                       int32_t* node_argmax, int32_t* accept_len, int32_t* accept_path);
+
 /* Bytes of workspace tree_attn_verify needs for this descriptor (0 if the
- * descriptor is invalid).  Pure host computation. */
+ * descriptor is invalid or takes the plain kernel): for the MFMA kernels,
+ * 256 bytes of work counters plus split-KV partials when the plan splits
+ * contexts.  Pure host computation. */
 size_t tree_attn_workspace_size(const tree_attn_desc* desc);
 
 /* Kernels tree_attn_verify launches for this descriptor on the current

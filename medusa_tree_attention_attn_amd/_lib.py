@@ -35,6 +35,7 @@ STATUS = {
 }
 EXPORTED = (
     "tree_attn_verify", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
+    "tree_vocab_argmax", "tree_argmax_accept",
     "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_plan_info", "tree_attn_rope_table",
     "tree_attn_strerror",
 )
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
         "tree_accept_greedy": (ctypes.c_int, [D, P, P, P, P, P]),
         "kv_commit_path": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
         "tree_accept_commit": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
+        "tree_vocab_argmax": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P]),
+        "tree_argmax_accept": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]),
         "tree_attn_workspace_size": (ctypes.c_size_t, [D]),
         "tree_attn_workspace_init": (ctypes.c_int, [D]),
         "tree_attn_plan_info": (ctypes.c_int, [D, P, P, P]),
@@ -230,6 +233,37 @@ def tree_accept_commit(desc, node_argmax, cand_tokens, tree_parent, accept_len, 
                                    _ptr(k_new), _ptr(v_new), _ptr(kv_pages), _ptr(block_table),
                                    _ptr(ctx_lens))
     _check(rc, "tree_accept_commit")
+
+
+def _logits_args(desc, logits):
+    B, T = desc.batch, desc.t_max
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TreeAttnError(-3, f"logits must be bfloat16 or float32, got {logits.dtype}")
+    if logits.dim() != 3 or tuple(logits.shape[:2]) != (B, T):
+        raise TreeAttnError(-2, f"logits must be [{B}][{T}][vocab], got {tuple(logits.shape)}")
+    _expect(logits, tuple(logits.shape), logits.dtype, "logits")
+    return (TA_BF16 if logits.dtype == torch.bfloat16 else TA_F32), int(logits.shape[2])
+
+
+def tree_vocab_argmax(desc, logits, node_argmax):
+    dt, V = _logits_args(desc, logits)
+    _expect(node_argmax, (desc.batch, desc.t_max), torch.int32, "node_argmax")
+    rc = load().tree_vocab_argmax(ctypes.byref(desc), _ptr(logits), dt, V, _ptr(node_argmax))
+    _check(rc, "tree_vocab_argmax")
+
+
+def tree_argmax_accept(desc, logits, cand_tokens, tree_parent, node_argmax, accept_len,
+                       accept_path):
+    dt, V = _logits_args(desc, logits)
+    B, T = desc.batch, desc.t_max
+    for t, shp, name in ((cand_tokens, (B, T), "cand_tokens"), (tree_parent, (B, T), "tree_parent"),
+                         (node_argmax, (B, T), "node_argmax"), (accept_len, (B,), "accept_len"),
+                         (accept_path, (B, T), "accept_path")):
+        _expect(t, shp, torch.int32, name)
+    rc = load().tree_argmax_accept(ctypes.byref(desc), _ptr(logits), dt, V, _ptr(cand_tokens),
+                                   _ptr(tree_parent), _ptr(node_argmax), _ptr(accept_len),
+                                   _ptr(accept_path))
+    _check(rc, "tree_argmax_accept")
 
 
 KERNEL_NAMES = {0: "verify_simple_kernel", 1: "verify_mfma_kernel", 2: "verify_stream_kernel"}

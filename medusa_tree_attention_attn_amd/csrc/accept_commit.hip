@@ -1,6 +1,7 @@
 // Greedy acceptance, KV commit, RoPE table and workspace fill kernels.
 #include <math.h>
 
+#include "accept.h"
 #include "launch.h"
 
 namespace ta {
@@ -15,55 +16,6 @@ namespace {
 //   accepted = every node on the root path is ok:  (anc_i & ~M) == 0
 //   end      = argmax over accepted nodes of (depth, -index)
 // ---------------------------------------------------------------------------
-struct Acceptance {
-  int len;          // accepted nodes, root included
-  uint64_t path;    // bit k set iff node k is on the accepted path
-  int depth;        // this lane's depth in the tree (meaningful on linked lanes)
-  bool in_tree;     // lane < T
-};
-
-// Called by one full wavefront; lane i evaluates node i of sequence b.
-__device__ __forceinline__ Acceptance accept_wave(const int32_t* __restrict__ node_argmax,
-                                                  const int32_t* __restrict__ cand_tokens,
-                                                  const int32_t* __restrict__ tree_parent, int b,
-                                                  int T, int i) {
-  const bool in_tree = i < T;
-  const size_t row = (size_t)b * T;
-  const int par = in_tree ? tree_parent[row + i] : kPadParent;
-  const bool linked = (i == 0) ? (par == -1) : (par >= 0 && par < i);
-  const bool ok = linked && (i == 0 || cand_tokens[row + i] == node_argmax[row + par]);
-  const uint64_t M = __ballot(ok);
-
-  uint64_t anc = linked ? (1ull << i) : 0ull;
-  int up = (linked && i > 0) ? par : i;  // the root (and unlinked lanes) point at themselves
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {          // 2^6 - 1 >= 63 levels
-    const uint64_t a_up = __shfl(anc, up);
-    const int up_up = __shfl(up, up);
-    anc |= a_up;
-    up = up_up;
-  }
-  const bool rooted = (anc & 1ull) != 0ull;
-  const bool accepted = linked && rooted && ((anc & ~M) == 0ull);
-  const int depth = __popcll(anc) - 1;
-  int key = accepted ? (depth << 6) | (63 - i) : -1;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
-  const int end = 63 - (key & 63);       // key >= 0: the root is always accepted
-  const uint64_t anc_end = __shfl(anc, end);
-  return Acceptance{(int)__popcll(anc_end), anc_end, depth, in_tree};
-}
-
-__device__ __forceinline__ void write_acceptance(const Acceptance& a, int32_t* accept_len,
-                                                 int32_t* accept_path, int b, int T, int i) {
-  const size_t row = (size_t)b * T;
-  if (a.in_tree) {
-    if ((a.path >> i) & 1ull) accept_path[row + a.depth] = i;
-    if (i >= a.len) accept_path[row + i] = -1;
-  }
-  if (i == 0) accept_len[b] = a.len;
-}
-
 __global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ node_argmax,
                                                     const int32_t* __restrict__ cand_tokens,
                                                     const int32_t* __restrict__ tree_parent,

@@ -208,6 +208,37 @@ int tree_accept_commit(const tree_attn_desc* d, const int32_t* node_argmax,
                                         static_cast<hipStream_t>(d->stream)));
 }
 
+int tree_vocab_argmax(const tree_attn_desc* d, const void* logits, int32_t logits_dtype,
+                      int32_t vocab, int32_t* node_argmax) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->t_max <= 0 || d->batch > 65535) return TA_ERR_BAD_DIMS;
+  if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  if (logits_dtype != TA_BF16 && logits_dtype != TA_F32) return TA_ERR_DTYPE;
+  if (vocab <= 0) return TA_ERR_BAD_DIMS;
+  if (!logits || !node_argmax) return TA_ERR_NULL_POINTER;
+  return status_of(launch_vocab_argmax(logits, logits_dtype, vocab, d->batch * d->t_max,
+                                       node_argmax, static_cast<hipStream_t>(d->stream)));
+}
+
+int tree_argmax_accept(const tree_attn_desc* d, const void* logits, int32_t logits_dtype,
+                       int32_t vocab, const int32_t* cand_tokens, const int32_t* tree_parent,
+                       int32_t* node_argmax, int32_t* accept_len, int32_t* accept_path) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->t_max <= 0 || d->batch > 65535) return TA_ERR_BAD_DIMS;
+  if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  if (logits_dtype != TA_BF16 && logits_dtype != TA_F32) return TA_ERR_DTYPE;
+  if (vocab <= 0) return TA_ERR_BAD_DIMS;
+  if (!logits || !cand_tokens || !tree_parent || !node_argmax || !accept_len || !accept_path)
+    return TA_ERR_NULL_POINTER;
+  hipStream_t stream = static_cast<hipStream_t>(d->stream);
+  hipError_t e = launch_vocab_argmax(logits, logits_dtype, vocab, d->batch * d->t_max,
+                                     node_argmax, stream);
+  if (e == hipSuccess)
+    e = launch_accept(node_argmax, cand_tokens, tree_parent, accept_len, accept_path, d->batch,
+                      d->t_max, stream);
+  return status_of(e);
+}
+
 int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* table,
                          void* stream) {
   if (!table) return TA_ERR_NULL_POINTER;

@@ -44,6 +44,10 @@ hipError_t launch_accept_commit(const CommitParams& p, const int32_t* node_argma
                                 int32_t* accept_len, int32_t* accept_path, int dtype,
                                 hipStream_t stream);
 
+// node_argmax[r] = argmax over V of row r of logits (rows x V, dtype TA_BF16
+// or TA_F32), smallest token among equal maxima.
+hipError_t launch_vocab_argmax(const void* logits, int dtype, int V, int rows, int32_t* out,
+                               hipStream_t stream);
 hipError_t launch_rope_table(int head_dim, float base, int max_pos, float* table,
                              hipStream_t stream);
 

@@ -64,12 +64,10 @@ inline Plan make_plan(const tree_attn_desc& d) {
   if (chunk > kMaxSplitTokens) chunk = kMaxSplitTokens;
   p.chunk = chunk;
   p.splits = (max_ctx + chunk - 1) / chunk;
-  if (!p.mfma) return p;
-  size_t off = 0;
-  if (p.stream) {
-    p.off_ctr = 0;
-    off = 256;
-  }
+  if (!p.mfma) return p;  // the plain kernel needs no workspace
+  // The persistent kernel's work counters (kept zero between calls).
+  p.off_ctr = 0;
+  size_t off = 256;
   if (p.splits > 1) {
     const size_t bh = (size_t)d.batch * d.num_heads;
     const size_t rows = bh * (size_t)p.splits * d.t_max;

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_commit,
-                   tree_accept_greedy,
+                   tree_accept_greedy, tree_argmax_accept, tree_vocab_argmax,
                    tree_attn_rope_table, tree_attn_verify, tree_attn_workspace_init,
                    tree_attn_workspace_size)
 
@@ -88,3 +88,27 @@ class TreeVerifier:
         tree_accept_commit(self.desc, node_argmax, cand_tokens, tree_parent, accept_len,
                            accept_path, k_new, v_new, kv_pages, block_table, ctx_lens)
         return accept_len, accept_path
+
+    def vocab_argmax(self, logits, node_argmax=None):
+        """Greedy token after every node: argmax of logits [B][T][V] over V."""
+        self._sync_stream()
+        if node_argmax is None:
+            node_argmax = torch.empty((self.desc.batch, self.desc.t_max), dtype=torch.int32,
+                                      device=self.device)
+        tree_vocab_argmax(self.desc, logits, node_argmax)
+        return node_argmax
+
+    def argmax_accept(self, logits, cand_tokens, tree_parent, node_argmax=None, accept_len=None,
+                      accept_path=None):
+        """vocab_argmax() then accept() of its result, in one library launch."""
+        self._sync_stream()
+        B, T = self.desc.batch, self.desc.t_max
+        if node_argmax is None:
+            node_argmax = torch.empty((B, T), dtype=torch.int32, device=self.device)
+        if accept_len is None:
+            accept_len = torch.empty((B,), dtype=torch.int32, device=self.device)
+        if accept_path is None:
+            accept_path = torch.empty((B, T), dtype=torch.int32, device=self.device)
+        tree_argmax_accept(self.desc, logits, cand_tokens, tree_parent, node_argmax, accept_len,
+                           accept_path)
+        return node_argmax, accept_len, accept_path

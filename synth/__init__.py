@@ -290,3 +290,28 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
                     node_argmax=amax, block_table=table, num_blocks=nblocks,
                     max_ctx_len=int(hi), q=q, k_new=k_new, v_new=v_new,
                     kv_pages=pool)
+
+
+def make_logits(wl: Workload, seed: int = 0, *, vocab: Optional[int] = None,
+                dtype: torch.dtype = torch.bfloat16, scale: float = 2.0,
+                planted_margin: float = 4.0, ties: int = 0) -> torch.Tensor:
+    """Base-model logits after every tree node, [B][T][vocab] on the CPU.
+
+    Values are scale * N(0,1) (drawn in fp32, rounded to `dtype`); in each row
+    the token wl.node_argmax[b][i] is then raised to the row's largest value
+    plus `planted_margin`, so the rows' greedy tokens are the workload's
+    planted ones (and acceptance sees the workload's match rate).  With
+    ties > 0, that many other random tokens of each row are set to the same
+    value, so equal maxima occur (the greedy token is then the smallest id
+    among them, no longer necessarily the planted one)."""
+    B, T = wl.node_argmax.shape
+    V = vocab or wl.spec.vocab
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x10C175]))
+    x = _normal(np.random.SeedSequence([seed, 0x10C176]), (B, T, V), torch.float32) * scale
+    top = x.max(dim=-1).values + planted_margin            # [B][T]
+    tok = torch.from_numpy(np.asarray(wl.node_argmax, dtype=np.int64) % V)
+    x.scatter_(-1, tok.unsqueeze(-1), top.unsqueeze(-1))
+    if ties > 0:
+        extra = torch.from_numpy(rng.integers(0, V, size=(B, T, ties)))
+        x.scatter_(-1, extra, top.unsqueeze(-1).expand(B, T, ties))
+    return x.to(dtype)

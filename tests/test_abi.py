@@ -135,6 +135,28 @@ def test_accept_commit_null_and_checks(lib, which):
     assert lib.tree_accept_commit(ctypes.byref(_desc()), *bad) == -12
 
 
+def test_argmax_entry_checks(lib):
+    good = [0x3000, 0, 32000, 0x4000]
+    d = ctypes.byref(_desc())
+    assert lib.tree_vocab_argmax(None, *good) == -1
+    assert lib.tree_vocab_argmax(d, None, 0, 32000, 0x4000) == -1
+    assert lib.tree_vocab_argmax(d, 0x3000, 0, 32000, None) == -1
+    assert lib.tree_vocab_argmax(d, 0x3000, 7, 32000, 0x4000) == -3     # dtype
+    assert lib.tree_vocab_argmax(d, 0x3000, 0, 0, 0x4000) == -2         # vocab
+    assert lib.tree_vocab_argmax(ctypes.byref(_desc(t_max=65)), *good) == -4
+    args = [0x3000, 0, 32000] + [0x4000 + 0x100 * i for i in range(5)]
+    for which in (0, 3, 4, 5, 6, 7):
+        bad = list(args)
+        bad[which] = None
+        assert lib.tree_argmax_accept(d, *bad) == -1
+    bad = list(args)
+    bad[1] = 2
+    assert lib.tree_argmax_accept(d, *bad) == -3
+    bad = list(args)
+    bad[2] = 0
+    assert lib.tree_argmax_accept(d, *bad) == -2
+
+
 def test_plan_info_follows_flags(lib):
     """The kernel choice is a host-side rule: forced by the flags, else the
     persistent kernel only with >= 4 work items per CU (no device here: 0 CUs,
@@ -193,9 +215,10 @@ def test_workspace_size_grows_with_context(lib):
                                                                max_ctx_len=4000,
                                                                max_blocks_per_seq=260,
                                                                rope_max_pos=4064)))
-    assert simple == 0
+    assert simple == 0                        # the plain kernel needs no workspace
     f32 = lib.tree_attn_workspace_size(ctypes.byref(_desc(dtype=ta.TA_F32)))
     assert f32 == 0
+    assert a == 256 and b > 256               # MFMA: work counters, then split partials
 
 
 def test_rope_table_errors(lib):
