@@ -199,13 +199,18 @@ def cpu_baseline_leg(wl, timed, posterior_out):
     import oracle
     parity = _oracle_parity(wl, *timed)
     if posterior_out is not None:
+        from oracle.candidates import assemble_candidates
         from oracle.posterior import vocab_argmax
-        logits, A, L, P = posterior_out
+        logits, A, L, P, (hl, choices, root, topk, C, Pc, Dc) = posterior_out
         ref = vocab_argmax(logits)
         Lr, Pr = oracle.accept_greedy(ref, wl.cand_tokens, wl.tree_parent)
         parity["posterior_bit_exact"] = bool(np.array_equal(A, ref) and np.array_equal(L, Lr)
                                              and np.array_equal(P, Pr))
-        parity["ok"] = parity["ok"] and parity["posterior_bit_exact"]
+        Cr, Pcr, Dcr = assemble_candidates(hl, choices, root, wl.spec.t_max, topk)
+        parity["candidates_bit_exact"] = bool(np.array_equal(C, Cr) and np.array_equal(Pc, Pcr)
+                                              and np.array_equal(Dc, Dcr))
+        parity["ok"] = (parity["ok"] and parity["posterior_bit_exact"]
+                        and parity["candidates_bit_exact"])
     return parity, _oracle_timing(wl)
 
 
@@ -268,8 +273,41 @@ def posterior_bench(wl, tv, dev, seed, log, reps=50):
         gbs = out["bytes_per_launch"] / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del xs
+    # Candidate tree for the next step: 4 Medusa heads' logits, a 63-path
+    # choices list (top-10 ranks, depth <= 4).
+    from synth import make_choices, make_head_logits
+    n_heads, topk = 4, 10
+    choices = make_choices(seed, n=63, max_depth=4, topk=topk)
+    hl = make_head_logits(B, n_heads, logits.shape[-1], seed=seed)
+    root = torch.from_numpy(np.asarray(wl.node_argmax[:, 0], dtype=np.int32))
+    hb = hl.numel() * hl.element_size()
+    hcopies = max(2, math.ceil(POOL_BYTES_TARGET / hb))
+    hs = [hl.to(dev) for _ in range(hcopies)]
+    root_d = root.to(dev)
+    C = torch.empty((B, T), dtype=torch.int32, device=dev)
+    Pc = torch.empty_like(C)
+    Dc = torch.empty_like(C)
+    fn = lambda x: tv.candidates(choices, x, topk, root_d, C, Pc, Dc)
+    for k in range(5):
+        fn(hs[k % hcopies])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(reps):
+        fn(hs[k % hcopies])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    out["medusa_candidates"] = {
+        "head_logits": f"bf16 [{B}][{n_heads}][{hl.shape[-1]}], {hcopies} rotating copies",
+        "choices": f"{len(choices)} paths, top-{topk}", "us": round(us, 2),
+        "GB/s": round(hb / (us * 1e-6) / 1e9, 1)}
+    del hs
     log(f"posterior: {out}")
-    return out, (logits, A.cpu().numpy(), L.cpu().numpy(), P.cpu().numpy())
+    return out, (logits, A.cpu().numpy(), L.cpu().numpy(), P.cpu().numpy(),
+                 (hl, choices, root.numpy(), topk, C.cpu().numpy(), Pc.cpu().numpy(),
+                  Dc.cpu().numpy()))
 
 
 def main():

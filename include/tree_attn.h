@@ -98,7 +98,8 @@ enum ta_status {
   TA_ERR_ROPE_TABLE = -9,     /* rope table missing or rope_max_pos too small*/
   TA_ERR_CAPACITY = -10,      /* max_blocks_per_seq*16 < max_ctx_len         */
   TA_ERR_LAUNCH = -11,        /* the HIP runtime rejected a launch           */
-  TA_ERR_ALIGNMENT = -12      /* a tensor pointer is not 16-byte aligned     */
+  TA_ERR_ALIGNMENT = -12,     /* a tensor pointer is not 16-byte aligned     */
+  TA_ERR_CHOICES = -13        /* a medusa choices list is not a valid tree   */
 };
 
 typedef struct tree_attn_desc {
@@ -214,6 +215,32 @@ int tree_vocab_argmax(const tree_attn_desc* desc, const void* logits, int32_t lo
 int tree_argmax_accept(const tree_attn_desc* desc, const void* logits, int32_t logits_dtype,
                        int32_t vocab, const int32_t* cand_tokens, const int32_t* tree_parent,
                        int32_t* node_argmax, int32_t* accept_len, int32_t* accept_path);
+
+/* Candidate tree from the Medusa heads (LMDeploy #1231 generate_candidates
+ * with a fixed "medusa choices" list).
+ *   choices      HOST int32 [n_choices][max_len]: each row a path of top-k
+ *                ranks (r_1, ..., r_d), -1 after its end.  The list must be
+ *                prefix-closed (every proper prefix is also a row), without
+ *                duplicates, with d <= num_medusa_heads and r < topk.
+ *   head_logits  device [B][num_medusa_heads][vocab] of head_dtype (TA_BF16
+ *                or TA_F32); head h predicts the token at depth h + 1.
+ *   root_token   device int32 [B]: the token decided by the previous step.
+ * Nodes are numbered root 0, then the paths by length, then
+ * lexicographically (node = 1 + position).  Writes, for every sequence:
+ *   cand_tokens[b][n]  root_token[b] for n = 0; for the path (r_1..r_d) the
+ *                      r_d-th best token of head d-1 (logit descending,
+ *                      smaller token among equal logits, NaN ranks as -inf);
+ *   tree_parent[b][n]  the node of (r_1..r_{d-1}) (-1 for the root);
+ *   tree_depth[b][n]   d;
+ * and padding (parent -2, depth 0, token 0) for n > n_choices up to t_max.
+ * Uses batch, t_max and stream of desc.  topk <= 16 and <= vocab;
+ * n_choices + 1 <= t_max.  An invalid list returns TA_ERR_CHOICES before
+ * anything is enqueued; other errors as tree_vocab_argmax. */
+int tree_medusa_candidates(const tree_attn_desc* desc, const int32_t* choices, int32_t n_choices,
+                           int32_t max_len, const void* head_logits, int32_t head_dtype,
+                           int32_t num_medusa_heads, int32_t vocab, int32_t topk,
+                           const int32_t* root_token, int32_t* cand_tokens, int32_t* tree_parent,
+                           int32_t* tree_depth);
 
 /* Bytes of workspace tree_attn_verify needs for this descriptor (0 if the
  * descriptor is invalid or takes the plain kernel): for the MFMA kernels,

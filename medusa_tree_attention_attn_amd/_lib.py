@@ -32,10 +32,11 @@ STATUS = {
     -4: "TA_ERR_TREE_TOO_LARGE", -5: "TA_ERR_HEAD_DIM", -6: "TA_ERR_HEADS",
     -7: "TA_ERR_BLOCK_SIZE", -8: "TA_ERR_WORKSPACE", -9: "TA_ERR_ROPE_TABLE",
     -10: "TA_ERR_CAPACITY", -11: "TA_ERR_LAUNCH", -12: "TA_ERR_ALIGNMENT",
+    -13: "TA_ERR_CHOICES",
 }
 EXPORTED = (
     "tree_attn_verify", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
-    "tree_vocab_argmax", "tree_argmax_accept",
+    "tree_vocab_argmax", "tree_argmax_accept", "tree_medusa_candidates",
     "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_plan_info", "tree_attn_rope_table",
     "tree_attn_strerror",
 )
@@ -91,6 +92,9 @@ def load() -> ctypes.CDLL:
         "tree_accept_commit": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
         "tree_vocab_argmax": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P]),
         "tree_argmax_accept": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]),
+        "tree_medusa_candidates": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P,
+                                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, P, P, P, P]),
         "tree_attn_workspace_size": (ctypes.c_size_t, [D]),
         "tree_attn_workspace_init": (ctypes.c_int, [D]),
         "tree_attn_plan_info": (ctypes.c_int, [D, P, P, P]),
@@ -264,6 +268,38 @@ def tree_argmax_accept(desc, logits, cand_tokens, tree_parent, node_argmax, acce
                                    _ptr(tree_parent), _ptr(node_argmax), _ptr(accept_len),
                                    _ptr(accept_path))
     _check(rc, "tree_argmax_accept")
+
+
+def choices_array(choices):
+    """A list of rank paths -> (int32 numpy [n][max_len] padded with -1)."""
+    import numpy as np
+    n = len(choices)
+    m = max((len(c) for c in choices), default=1)
+    a = np.full((max(n, 1), m), -1, dtype=np.int32)
+    for i, c in enumerate(choices):
+        a[i, :len(c)] = c
+    return a
+
+
+def tree_medusa_candidates(desc, choices, head_logits, topk, root_token, cand_tokens,
+                           tree_parent, tree_depth):
+    import numpy as np
+    B, T = desc.batch, desc.t_max
+    if head_logits.dtype not in (torch.bfloat16, torch.float32) or head_logits.dim() != 3 \
+            or head_logits.shape[0] != B:
+        raise TreeAttnError(-2, f"head_logits must be [{B}][heads][vocab] bf16/fp32")
+    _expect(head_logits, tuple(head_logits.shape), head_logits.dtype, "head_logits")
+    _expect(root_token, (B,), torch.int32, "root_token")
+    for t, name in ((cand_tokens, "cand_tokens"), (tree_parent, "tree_parent"),
+                    (tree_depth, "tree_depth")):
+        _expect(t, (B, T), torch.int32, name)
+    arr = np.ascontiguousarray(choices_array(choices))
+    rc = load().tree_medusa_candidates(
+        ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p), len(choices), arr.shape[1],
+        _ptr(head_logits), TA_BF16 if head_logits.dtype == torch.bfloat16 else TA_F32,
+        int(head_logits.shape[1]), int(head_logits.shape[2]), int(topk), _ptr(root_token),
+        _ptr(cand_tokens), _ptr(tree_parent), _ptr(tree_depth))
+    _check(rc, "tree_medusa_candidates")
 
 
 KERNEL_NAMES = {0: "verify_simple_kernel", 1: "verify_mfma_kernel", 2: "verify_stream_kernel"}

@@ -1,7 +1,8 @@
-// Greedy acceptance of one sequence's tree by one wavefront (LMDeploy PR
-// #1231 evaluate_posterior at LM-head temperature 0), shared by the kernels
-// that end in an acceptance.  Lane i = tree node i:
-//   ok_i     = edge parent(i) -> i matches (the root is always ok)
+// Acceptance of one sequence's tree by one wavefront (LMDeploy PR #1231
+// evaluate_posterior), shared by the kernels that end in an acceptance.
+// Lane i = tree node i:
+//   ok_i     = edge parent(i) -> i passes its test (the root is always ok):
+//              greedy token match, or the typical-acceptance threshold
 //   M        = ballot(ok)
 //   anc_i    = ancestor-or-self set of i, by pointer doubling over the lanes
 //   accepted = every node on the root path is ok:  (anc_i & ~M) == 0
@@ -19,16 +20,13 @@ struct Acceptance {
   bool in_tree;     // lane < T
 };
 
-// Called by one full wavefront; lane i evaluates node i of sequence b.
-__device__ __forceinline__ Acceptance accept_wave(const int32_t* __restrict__ node_argmax,
-                                                  const int32_t* __restrict__ cand_tokens,
-                                                  const int32_t* __restrict__ tree_parent, int b,
-                                                  int T, int i) {
-  const bool in_tree = i < T;
-  const size_t row = (size_t)b * T;
-  const int par = in_tree ? tree_parent[row + i] : kPadParent;
+// The accepted path of one tree, given each lane's (node's) parent and
+// whether its edge passed the test (`edge_ok`; the root's is ignored).
+// Called by one full wavefront; lane i = node i (lanes >= T: in_tree false,
+// parent kPadParent).
+__device__ __forceinline__ Acceptance select_path(int par, bool edge_ok, bool in_tree, int i) {
   const bool linked = (i == 0) ? (par == -1) : (par >= 0 && par < i);
-  const bool ok = linked && (i == 0 || cand_tokens[row + i] == node_argmax[row + par]);
+  const bool ok = linked && (i == 0 || edge_ok);
   const uint64_t M = __ballot(ok);
 
   uint64_t anc = linked ? (1ull << i) : 0ull;
@@ -49,6 +47,20 @@ __device__ __forceinline__ Acceptance accept_wave(const int32_t* __restrict__ no
   const int end = 63 - (key & 63);       // key >= 0: the root is always accepted
   const uint64_t anc_end = __shfl(anc, end);
   return Acceptance{(int)__popcll(anc_end), anc_end, depth, in_tree};
+}
+
+// Greedy acceptance: edge parent(i) -> i passes iff cand_tokens[i] equals
+// the base model's greedy token after the parent.
+__device__ __forceinline__ Acceptance accept_wave(const int32_t* __restrict__ node_argmax,
+                                                  const int32_t* __restrict__ cand_tokens,
+                                                  const int32_t* __restrict__ tree_parent, int b,
+                                                  int T, int i) {
+  const bool in_tree = i < T;
+  const size_t row = (size_t)b * T;
+  const int par = in_tree ? tree_parent[row + i] : kPadParent;
+  const bool linked = (i == 0) ? (par == -1) : (par >= 0 && par < i);
+  const bool match = linked && i > 0 && cand_tokens[row + i] == node_argmax[row + par];
+  return select_path(par, match, in_tree, i);
 }
 
 __device__ __forceinline__ void write_acceptance(const Acceptance& a, int32_t* accept_len,

@@ -3,6 +3,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <map>
+#include <vector>
+
 #include "launch.h"
 #include "plan.h"
 
@@ -239,6 +243,60 @@ int tree_argmax_accept(const tree_attn_desc* d, const void* logits, int32_t logi
   return status_of(e);
 }
 
+int tree_medusa_candidates(const tree_attn_desc* d, const int32_t* choices, int32_t n_choices,
+                           int32_t max_len, const void* head_logits, int32_t head_dtype,
+                           int32_t num_medusa_heads, int32_t vocab, int32_t topk,
+                           const int32_t* root_token, int32_t* cand_tokens, int32_t* tree_parent,
+                           int32_t* tree_depth) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->t_max <= 0 || d->batch > 65535) return TA_ERR_BAD_DIMS;
+  if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  if (head_dtype != TA_BF16 && head_dtype != TA_F32) return TA_ERR_DTYPE;
+  if (!head_logits || !root_token || !cand_tokens || !tree_parent || !tree_depth ||
+      (n_choices > 0 && !choices))
+    return TA_ERR_NULL_POINTER;
+  if (num_medusa_heads <= 0 || num_medusa_heads > 65535 || vocab <= 0 || topk <= 0 ||
+      topk > kMaxTopK || topk > vocab || n_choices < 0 || max_len <= 0)
+    return TA_ERR_BAD_DIMS;
+  if (n_choices + 1 > d->t_max) return TA_ERR_TREE_TOO_LARGE;
+  // Paths (host memory), validated and numbered: root 0, then by length,
+  // then lexicographically.
+  std::vector<std::vector<int>> paths(n_choices);
+  for (int c = 0; c < n_choices; ++c) {
+    for (int j = 0; j < max_len; ++j) {
+      const int r = choices[(size_t)c * max_len + j];
+      if (r < 0) break;
+      if (r >= topk) return TA_ERR_CHOICES;
+      paths[c].push_back(r);
+    }
+    if (paths[c].empty() || (int)paths[c].size() > num_medusa_heads) return TA_ERR_CHOICES;
+    for (int j = (int)paths[c].size(); j < max_len; ++j)
+      if (choices[(size_t)c * max_len + j] >= 0) return TA_ERR_CHOICES;  // gap in a path
+  }
+  std::sort(paths.begin(), paths.end(), [](const std::vector<int>& a, const std::vector<int>& b) {
+    return a.size() != b.size() ? a.size() < b.size() : a < b;
+  });
+  std::map<std::vector<int>, int> node_of;
+  node_of[{}] = 0;
+  CandTree tree{};
+  tree.n_nodes = n_choices + 1;
+  tree.parent[0] = -1;
+  for (int c = 0; c < n_choices; ++c) {
+    const std::vector<int>& p = paths[c];
+    if (node_of.count(p)) return TA_ERR_CHOICES;  // duplicate
+    const std::vector<int> up(p.begin(), p.end() - 1);
+    const auto it = node_of.find(up);
+    if (it == node_of.end()) return TA_ERR_CHOICES;  // prefix missing
+    node_of[p] = c + 1;
+    tree.parent[c + 1] = (int8_t)it->second;
+    tree.depth[c + 1] = (int8_t)p.size();
+    tree.rank[c + 1] = (int8_t)p.back();
+  }
+  return status_of(launch_candidates(head_logits, head_dtype, vocab, num_medusa_heads, topk, tree,
+                                     root_token, cand_tokens, tree_parent, tree_depth, d->batch,
+                                     d->t_max, static_cast<hipStream_t>(d->stream)));
+}
+
 int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* table,
                          void* stream) {
   if (!table) return TA_ERR_NULL_POINTER;
@@ -263,6 +321,7 @@ const char* tree_attn_strerror(int status) {
     case TA_ERR_CAPACITY: return "max_blocks_per_seq * 16 < max_ctx_len";
     case TA_ERR_LAUNCH: return "kernel launch failed";
     case TA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+    case TA_ERR_CHOICES: return "the medusa choices list is not a valid tree";
     default: return "unknown status";
   }
 }

@@ -48,6 +48,29 @@ hipError_t launch_accept_commit(const CommitParams& p, const int32_t* node_argma
 // or TA_F32), smallest token among equal maxima.
 hipError_t launch_vocab_argmax(const void* logits, int dtype, int V, int rows, int32_t* out,
                                hipStream_t stream);
+// Typical acceptance: per-node (log-sum-exp of logits / temperature,
+// entropy) into node_stats [rows][2], then the threshold test and the path.
+hipError_t launch_typical_accept(const void* logits, int dtype, int V, int B, int T,
+                                 float temperature, float epsilon, float delta,
+                                 const int32_t* cand_tokens, const int32_t* tree_parent,
+                                 float* node_stats, int32_t* node_ok, int32_t* accept_len,
+                                 int32_t* accept_path, hipStream_t stream);
+
+// Candidate tree from the Medusa heads: the node table of a validated
+// "medusa choices" list (root 0, then paths by length, then lexicographic),
+// passed by value.  rank[n] = last rank of node n's path (its token is the
+// rank-th best of head depth[n] - 1).
+constexpr int kMaxTopK = 16;
+struct CandTree {
+  int32_t n_nodes;          // root + choices, <= kMaxTree
+  int8_t parent[kMaxTree];
+  int8_t depth[kMaxTree];
+  int8_t rank[kMaxTree];
+};
+hipError_t launch_candidates(const void* head_logits, int dtype, int V, int n_heads, int topk,
+                             const CandTree& tree, const int32_t* root_token, int32_t* cand,
+                             int32_t* parent, int32_t* depth, int B, int T, hipStream_t stream);
+
 hipError_t launch_rope_table(int head_dim, float base, int max_pos, float* table,
                              hipStream_t stream);
 

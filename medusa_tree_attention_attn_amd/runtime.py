@@ -14,7 +14,8 @@ import torch
 
 from . import _lib
 from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_commit,
-                   tree_accept_greedy, tree_argmax_accept, tree_vocab_argmax,
+                   tree_accept_greedy, tree_argmax_accept, tree_medusa_candidates,
+                   tree_vocab_argmax,
                    tree_attn_rope_table, tree_attn_verify, tree_attn_workspace_init,
                    tree_attn_workspace_size)
 
@@ -112,3 +113,18 @@ class TreeVerifier:
         tree_argmax_accept(self.desc, logits, cand_tokens, tree_parent, node_argmax, accept_len,
                            accept_path)
         return node_argmax, accept_len, accept_path
+
+    def candidates(self, choices, head_logits, topk, root_token, cand_tokens=None,
+                   tree_parent=None, tree_depth=None):
+        """Candidate tree from Medusa head logits [B][heads][vocab] laid out by a
+        medusa-choices list (paths of top-k ranks); returns (cand_tokens,
+        tree_parent, tree_depth)."""
+        self._sync_stream()
+        B, T = self.desc.batch, self.desc.t_max
+        mk = lambda: torch.empty((B, T), dtype=torch.int32, device=self.device)
+        cand_tokens = mk() if cand_tokens is None else cand_tokens
+        tree_parent = mk() if tree_parent is None else tree_parent
+        tree_depth = mk() if tree_depth is None else tree_depth
+        tree_medusa_candidates(self.desc, choices, head_logits, topk, root_token, cand_tokens,
+                               tree_parent, tree_depth)
+        return cand_tokens, tree_parent, tree_depth

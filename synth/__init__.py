@@ -315,3 +315,39 @@ def make_logits(wl: Workload, seed: int = 0, *, vocab: Optional[int] = None,
         extra = torch.from_numpy(rng.integers(0, V, size=(B, T, ties)))
         x.scatter_(-1, extra, top.unsqueeze(-1).expand(B, T, ties))
     return x.to(dtype)
+
+
+def make_choices(seed: int = 0, n: int = 63, max_depth: int = 4, topk: int = 10):
+    """A synthetic "medusa choices" list: n distinct paths of top-k ranks,
+    prefix-closed (every path's prefixes are in the list), at most max_depth
+    long.  Grown from the root: a random existing node (the root or a path
+    shorter than max_depth, shallower ones more likely) gets its next child
+    rank (0, 1, 2, ... up to topk - 1), as lists tuned for an acceptance rate
+    favour the heads' best ranks."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xC401CE]))
+    children = {(): 0}
+    paths = []
+    while len(paths) < n:
+        open_nodes = [p for p in children if len(p) < max_depth and children[p] < topk]
+        w = np.array([0.5 ** len(p) for p in open_nodes])
+        p = open_nodes[int(rng.choice(len(open_nodes), p=w / w.sum()))]
+        c = p + (children[p],)
+        children[p] += 1
+        children[c] = 0
+        paths.append(c)
+    return paths
+
+
+def make_head_logits(batch: int, heads: int, vocab: int, seed: int = 0,
+                     dtype: torch.dtype = torch.bfloat16, ties: int = 0) -> torch.Tensor:
+    """Medusa head logits [batch][heads][vocab]: 2 * N(0,1) drawn in fp32 and
+    rounded to `dtype`; with ties > 0, each row's maximum is copied to that
+    many random other tokens (equal logits among the top)."""
+    x = _normal(np.random.SeedSequence([seed, 0x4EAD5]), (batch, heads, vocab),
+                torch.float32) * 2.0
+    if ties > 0:
+        rng = np.random.default_rng(np.random.SeedSequence([seed, 0x4EAD6]))
+        top = x.max(dim=-1).values
+        extra = torch.from_numpy(rng.integers(0, vocab, size=(batch, heads, ties)))
+        x.scatter_(-1, extra, top.unsqueeze(-1).expand(batch, heads, ties))
+    return x.to(dtype)

@@ -157,6 +157,35 @@ def test_argmax_entry_checks(lib):
     assert lib.tree_argmax_accept(d, *bad) == -2
 
 
+def _cand_rc(lib, choices, topk=10, heads=4, vocab=32000, t_max=64, n=None):
+    import numpy as np
+    from medusa_tree_attention_attn_amd._lib import choices_array
+    arr = np.ascontiguousarray(choices_array(choices))
+    return lib.tree_medusa_candidates(
+        ctypes.byref(_desc(t_max=t_max)), arr.ctypes.data_as(ctypes.c_void_p),
+        len(choices) if n is None else n, arr.shape[1], 0x3000, 0, heads, vocab, topk,
+        0x4000, 0x5000, 0x6000, 0x7000)
+
+
+def test_medusa_choices_validated_on_host(lib):
+    """Every rejection happens before anything is enqueued (no device here)."""
+    assert _cand_rc(lib, [(0,), (0,)]) == -13                  # duplicate path
+    assert _cand_rc(lib, [(0,), (1, 0)]) == -13                # prefix (1,) missing
+    assert _cand_rc(lib, [(0,), (10,)]) == -13                 # rank >= topk
+    assert _cand_rc(lib, [(0,), (0, 0), (0, 0, 0), (0, 0, 0, 0), (0, 0, 0, 0, 0)]) == -13  # deeper than 4 heads
+    assert _cand_rc(lib, [(0,), (0, 0)], t_max=2) == -4       # 3 nodes > t_max
+    assert _cand_rc(lib, [(0,)], topk=17) == -2                # topk > 16
+    assert _cand_rc(lib, [(0,)], topk=8, vocab=7) == -2        # topk > vocab
+    import numpy as np
+    gap = np.array([[0, -1, 1]], dtype=np.int32)               # -1 then a rank
+    assert lib.tree_medusa_candidates(ctypes.byref(_desc()), gap.ctypes.data_as(ctypes.c_void_p),
+                                      1, 3, 0x3000, 0, 4, 100, 4, 0x4000, 0x5000, 0x6000,
+                                      0x7000) == -13
+    assert lib.tree_medusa_candidates(ctypes.byref(_desc()), None, 1, 1, 0x3000, 0, 4, 100, 4,
+                                      0x4000, 0x5000, 0x6000, 0x7000) == -1
+    assert _cand_rc(lib, [(0,)], heads=0) == -2
+
+
 def test_plan_info_follows_flags(lib):
     """The kernel choice is a host-side rule: forced by the flags, else the
     persistent kernel only with >= 4 work items per CU (no device here: 0 CUs,
