@@ -112,6 +112,9 @@ def write_traffic_record(fetch_csv: str, write_csv: str, workload: str, seed: in
 
 
 POOL_BYTES_TARGET = 1 << 30
+# Typical acceptance settings measured and checked: temperature, epsilon
+# (posterior threshold) and delta (its entropy factor), as commonly set for Medusa.
+TYPICAL = (1.0, 0.09, 0.3)
 
 
 def algorithmic_bytes(wl, accept_len=None):
@@ -201,17 +204,59 @@ def cpu_baseline_leg(wl, timed, posterior_out):
     if posterior_out is not None:
         from oracle.candidates import assemble_candidates
         from oracle.posterior import vocab_argmax
-        logits, A, L, P, (hl, choices, root, topk, C, Pc, Dc) = posterior_out
+        logits = posterior_out["logits"]
+        A, L, P = posterior_out["greedy"]
         ref = vocab_argmax(logits)
         Lr, Pr = oracle.accept_greedy(ref, wl.cand_tokens, wl.tree_parent)
         parity["posterior_bit_exact"] = bool(np.array_equal(A, ref) and np.array_equal(L, Lr)
                                              and np.array_equal(P, Pr))
+        parity["typical"] = _typical_parity(wl, logits, *posterior_out["typical"])
+        hl, choices, root, topk, C, Pc, Dc = posterior_out["candidates"]
         Cr, Pcr, Dcr = assemble_candidates(hl, choices, root, wl.spec.t_max, topk)
         parity["candidates_bit_exact"] = bool(np.array_equal(C, Cr) and np.array_equal(Pc, Pcr)
                                               and np.array_equal(Dc, Dcr))
         parity["ok"] = (parity["ok"] and parity["posterior_bit_exact"]
-                        and parity["candidates_bit_exact"])
+                        and parity["typical"]["ok"] and parity["candidates_bit_exact"])
     return parity, _oracle_timing(wl)
+
+
+def _typical_parity(wl, logits, S, OK, L, P):
+    """Typical acceptance against the oracle: per-node (lse, entropy) within
+    1e-4, per-child results exact outside a relative 1e-4 band around the
+    threshold, and the path exactly the oracle's rule over the GPU's own
+    per-child results."""
+    from oracle.posterior import _longest_path, softmax_stats, typical_accept
+    temp, eps, delta = TYPICAL
+    par = np.asarray(wl.tree_parent)
+    cand = np.asarray(wl.cand_tokens)
+    p, H = softmax_stats(logits, temp)
+    x = logits.to(torch.float64).numpy() / temp
+    m = x.max(axis=-1)
+    lse = m + np.log(np.exp(x - m[..., None]).sum(axis=-1))
+    del x
+    Lr, Pr, okr = typical_accept(logits, cand, par, temp, eps, delta)
+    thr = np.minimum(eps, delta * np.exp(-H))
+    B, T = par.shape
+    near = np.zeros((B, T), dtype=bool)
+    for b in range(B):
+        for i in range(1, T):
+            n = par[b, i]
+            if n >= 0:
+                near[b, i] = abs(p[b, n, cand[b, i]] - thr[b, n]) <= 1e-4 * thr[b, n]
+    del p
+    err_lse = float(np.abs(S[..., 0] - lse).max())
+    err_h = float(np.abs(S[..., 1] - H).max())
+    ok_nodes = bool(np.array_equal(OK[~near], okr[~near].astype(np.int32)))
+    Lg, Pg = _longest_path(OK.astype(bool), par)
+    ok_path = bool(np.array_equal(L, Lg) and np.array_equal(P, Pg))
+    clean = ~near.any(axis=1)
+    ok_oracle_path = bool(np.array_equal(L[clean], Lr[clean]) and
+                          np.array_equal(P[clean], Pr[clean]))
+    return dict(lse_max_abs_err=err_lse, entropy_max_abs_err=err_h,
+                nodes_near_threshold=int(near.sum()), node_ok_exact=ok_nodes,
+                path_exact=ok_path and ok_oracle_path,
+                ok=bool(err_lse <= 1e-4 + 1e-5 * np.abs(lse).max() and err_h <= 1e-4 + 1e-5 *
+                        np.abs(H).max() and ok_nodes and ok_path and ok_oracle_path))
 
 
 def _oracle_timing(wl):
@@ -239,13 +284,56 @@ def _oracle_timing(wl):
                 seconds=dt)
 
 
+def time_calls(fn, n_inputs, reps, outputs):
+    """Average microseconds per call of fn(k) (k picks input k % n_inputs):
+      eager  back-to-back calls from Python between two events: what a
+             caller sees, host overhead included when it exceeds the GPU's
+             share;
+      gpu    the same calls captured once into a HIP graph and replayed:
+             the kernels' own time (launch gaps of a replayed graph only).
+    The graph's outputs after the replay must equal the eager ones (both
+    end on the same input); otherwise gpu is None."""
+    for k in range(5):
+        fn(k % n_inputs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(reps):
+        fn(k % n_inputs)
+    b.record()
+    torch.cuda.synchronize()
+    eager = a.elapsed_time(b) * 1e3 / reps
+    ref = [t.clone() for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(reps):
+            fn(k % n_inputs)
+    torch.cuda.synchronize()
+    gpu = []
+    for _ in range(3):
+        for t in outputs:
+            t.fill_(-7)          # replays must rewrite every output
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        if not all(torch.equal(t, r) for t, r in zip(outputs, ref)):
+            return round(eager, 2), None
+        gpu.append(a.elapsed_time(b) * 1e3 / reps)
+    del g
+    return round(eager, 2), round(min(gpu), 2)
+
+
 def posterior_bench(wl, tv, dev, seed, log, reps=50):
     """The greedy token of every node from synthetic bf16 logits [B][T][vocab]
-    (tree_vocab_argmax) and the same fused with acceptance
-    (tree_argmax_accept): launch time back to back over rotating copies
-    (>= 1 GB, beyond the Infinity Cache), and the HBM fraction of the
-    logits stream.  Returns the figures and (logits, node_argmax, accept_len,
-    accept_path) of the last fused call for the oracle leg to check."""
+    (tree_vocab_argmax), the same fused with acceptance
+    (tree_argmax_accept), typical acceptance (tree_accept_typical) and the
+    next step's candidate tree (tree_medusa_candidates), each over rotating
+    input copies (>= 1 GB, beyond the Infinity Cache), timed eager and as a
+    replayed graph (time_calls), with the HBM fraction of the input stream
+    at the graph's time.  Returns the figures and the outputs of the last
+    calls for the oracle leg to check."""
     from synth import make_logits
     logits = make_logits(wl, seed)
     nb = logits.numel() * logits.element_size()
@@ -256,29 +344,32 @@ def posterior_bench(wl, tv, dev, seed, log, reps=50):
     A = torch.empty((B, T), dtype=torch.int32, device=dev)
     L = torch.empty((B,), dtype=torch.int32, device=dev)
     P = torch.empty((B, T), dtype=torch.int32, device=dev)
+    S = torch.empty((B, T, 2), dtype=torch.float32, device=dev)
+    OK = torch.empty((B, T), dtype=torch.int32, device=dev)
+    Lt, Pt = torch.empty_like(L), torch.empty_like(P)
     out = {"logits": f"bf16 [{B}][{T}][{logits.shape[-1]}], {copies} rotating copies",
            "bytes_per_launch": nb + B * T * 4}
-    for name, fn in (("vocab_argmax", lambda x: tv.vocab_argmax(x, A)),
-                     ("argmax_accept", lambda x: tv.argmax_accept(x, cand, par, A, L, P))):
-        for k in range(5):
-            fn(xs[k % copies])
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for k in range(reps):
-            fn(xs[k % copies])
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / reps
-        gbs = out["bytes_per_launch"] / (us * 1e-6) / 1e9
-        out[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
-                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    def record(name, eager, gpu, nbytes):
+        us = gpu if gpu is not None else eager
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "eager_us": eager, "graph": gpu is not None,
+                     "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    temp, eps, delta = TYPICAL
+    for name, fn, outs in (
+            ("vocab_argmax", lambda k: tv.vocab_argmax(xs[k], A), [A]),
+            ("argmax_accept", lambda k: tv.argmax_accept(xs[k], cand, par, A, L, P), [A, L, P]),
+            ("typical_accept", lambda k: tv.accept_typical(xs[k], cand, par, temp, eps, delta,
+                                                           S, OK, Lt, Pt), [S, OK, Lt, Pt])):
+        record(name, *time_calls(fn, copies, reps, outs), out["bytes_per_launch"])
     del xs
     # Candidate tree for the next step: 4 Medusa heads' logits, a 63-path
-    # choices list (top-10 ranks, depth <= 4).
+    # choices list (top-10 ranks, depth <= 4) numbered once.
     from synth import make_choices, make_head_logits
     n_heads, topk = 4, 10
     choices = make_choices(seed, n=63, max_depth=4, topk=topk)
+    table = tv.medusa_tree(choices, topk, n_heads)
     hl = make_head_logits(B, n_heads, logits.shape[-1], seed=seed)
     root = torch.from_numpy(np.asarray(wl.node_argmax[:, 0], dtype=np.int32))
     hb = hl.numel() * hl.element_size()
@@ -288,26 +379,18 @@ def posterior_bench(wl, tv, dev, seed, log, reps=50):
     C = torch.empty((B, T), dtype=torch.int32, device=dev)
     Pc = torch.empty_like(C)
     Dc = torch.empty_like(C)
-    fn = lambda x: tv.candidates(choices, x, topk, root_d, C, Pc, Dc)
-    for k in range(5):
-        fn(hs[k % hcopies])
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for k in range(reps):
-        fn(hs[k % hcopies])
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
-    out["medusa_candidates"] = {
-        "head_logits": f"bf16 [{B}][{n_heads}][{hl.shape[-1]}], {hcopies} rotating copies",
-        "choices": f"{len(choices)} paths, top-{topk}", "us": round(us, 2),
-        "GB/s": round(hb / (us * 1e-6) / 1e9, 1)}
+    record("medusa_candidates",
+           *time_calls(lambda k: tv.candidates(table, hs[k], topk, root_d, C, Pc, Dc), hcopies,
+                       reps, [C, Pc, Dc]), hb + 3 * B * T * 4)
+    out["medusa_candidates"].update(
+        head_logits=f"bf16 [{B}][{n_heads}][{hl.shape[-1]}], {hcopies} rotating copies",
+        choices=f"{len(choices)} paths, top-{topk}")
     del hs
     log(f"posterior: {out}")
-    return out, (logits, A.cpu().numpy(), L.cpu().numpy(), P.cpu().numpy(),
-                 (hl, choices, root.numpy(), topk, C.cpu().numpy(), Pc.cpu().numpy(),
-                  Dc.cpu().numpy()))
+    host = lambda t: t.cpu().numpy()
+    return out, dict(logits=logits, greedy=(host(A), host(L), host(P)),
+                     typical=(host(S), host(OK), host(Lt), host(Pt)),
+                     candidates=(hl, choices, root.numpy(), topk, host(C), host(Pc), host(Dc)))
 
 
 def main():
@@ -433,6 +516,11 @@ def main():
     vb.record()
     torch.cuda.synchronize()
     ac_avg = va.elapsed_time(vb) / nv
+    # The same acceptance + commit launches as a replayed graph: the GPU's
+    # own time per call (the eager figure above is host-bound when the
+    # kernel is shorter than the Python call).
+    ac_gpu = None if args.separate_accept_commit else \
+        time_calls(accept_commit, copies, nv, [L, P])[1]
     # restore the outputs of the step loop's last step for the parity check
     step(args.warmup + args.steps - 1)
     torch.cuda.synchronize()
@@ -501,7 +589,8 @@ def main():
         "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
         "per_call_us": {"verify": round(v_avg * 1e3, 2),
                         ("accept, commit" if args.separate_accept_commit else "accept_commit"):
-                            round(ac_avg * 1e3, 2)},
+                            round(ac_avg * 1e3, 2),
+                        "accept_commit_graph": ac_gpu},
         "parity": {k: v for k, v in chk.items() if k not in ("ok", "sampled_sequences")},
         "posterior": posterior,
         "cpu_baseline": cpu,

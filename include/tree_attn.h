@@ -98,7 +98,7 @@ enum ta_status {
   TA_ERR_ROPE_TABLE = -9,     /* rope table missing or rope_max_pos too small*/
   TA_ERR_CAPACITY = -10,      /* max_blocks_per_seq*16 < max_ctx_len         */
   TA_ERR_LAUNCH = -11,        /* the HIP runtime rejected a launch           */
-  TA_ERR_ALIGNMENT = -12,     /* a tensor pointer is not 16-byte aligned     */
+  TA_ERR_ALIGNMENT = -12,     /* a pointer is not aligned as the call needs  */
   TA_ERR_CHOICES = -13        /* a medusa choices list is not a valid tree   */
 };
 
@@ -216,28 +216,69 @@ int tree_argmax_accept(const tree_attn_desc* desc, const void* logits, int32_t l
                        int32_t vocab, const int32_t* cand_tokens, const int32_t* tree_parent,
                        int32_t* node_argmax, int32_t* accept_len, int32_t* accept_path);
 
-/* Candidate tree from the Medusa heads (LMDeploy #1231 generate_candidates
- * with a fixed "medusa choices" list).
- *   choices      HOST int32 [n_choices][max_len]: each row a path of top-k
- *                ranks (r_1, ..., r_d), -1 after its end.  The list must be
- *                prefix-closed (every proper prefix is also a row), without
- *                duplicates, with d <= num_medusa_heads and r < topk.
+/* Typical acceptance (the Medusa scheme vLLM issue #1171 names as one of the
+ * two non-standard parts of Medusa serving; the rule is the Medusa paper's).
+ * For every node row r = (b, i), with y = logits[b][i][.] / temperature:
+ *   node_stats[r][0] = lse = log sum_v exp(y_v)           (natural log)
+ *   node_stats[r][1] = H   = -sum_v p_v log p_v,  p = softmax(y)
+ * (all B * t_max rows, padding included).  Child c of node n passes iff
+ *   exp(logits[b][n][cand_tokens[b][c]] / temperature - lse_n)
+ *       > min(epsilon, delta * exp(-H_n));
+ * node_ok[b][i] = 1 for the root and for every in-tree child that passes,
+ * 0 otherwise (padding, unlinked nodes, tokens outside [0, vocab)).  The
+ * accepted path is the deepest node whose whole root path passes (smallest
+ * index among equals), written to accept_len / accept_path with the
+ * conventions of tree_accept_greedy.  Arithmetic is fp32 (exp/log on the
+ * hardware units): a child whose probability lies within a few ulps of the
+ * threshold may go either way.  logits is a device tensor
+ * [B][t_max][vocab] of logits_dtype (TA_BF16 or TA_F32); node_stats is a
+ * device float [B][t_max][2], 8-byte aligned.  Two kernels on desc->stream.
+ * Errors: TA_ERR_NULL_POINTER, TA_ERR_BAD_DIMS (also temperature <= 0 or a
+ * non-finite temperature, epsilon or delta), TA_ERR_TREE_TOO_LARGE,
+ * TA_ERR_DTYPE, TA_ERR_ALIGNMENT, TA_ERR_LAUNCH. */
+int tree_accept_typical(const tree_attn_desc* desc, const void* logits, int32_t logits_dtype,
+                        int32_t vocab, const int32_t* cand_tokens, const int32_t* tree_parent,
+                        float temperature, float epsilon, float delta, float* node_stats,
+                        int32_t* node_ok, int32_t* accept_len, int32_t* accept_path);
+
+/* Node table of a fixed "medusa choices" list (LMDeploy #1231: the tree
+ * buffers built once from the list), on the host; no GPU work.
+ *   choices     HOST int32 [n_choices][max_len]: each row a path of top-k
+ *               ranks (r_1, ..., r_d), -1 after its end.  The list must be
+ *               prefix-closed (every proper prefix is also a row), without
+ *               duplicates, with d <= num_medusa_heads and r < topk.
+ *   node_table  HOST int32 [3][n_choices + 1], written: row 0 the parent,
+ *               row 1 the depth, row 2 the rank r_d of every node (root:
+ *               -1, 0, 0).  Nodes are numbered root 0, then the paths by
+ *               length, then lexicographically (node = 1 + position).
+ *   n_nodes     HOST int32, written: n_choices + 1.
+ * Errors: TA_ERR_NULL_POINTER, TA_ERR_BAD_DIMS (topk outside [1, 16],
+ * num_medusa_heads <= 0, n_choices < 0, max_len <= 0),
+ * TA_ERR_TREE_TOO_LARGE (more than 64 nodes), TA_ERR_CHOICES (an invalid
+ * list); node_table and n_nodes are untouched on error. */
+int tree_medusa_tree(const int32_t* choices, int32_t n_choices, int32_t max_len, int32_t topk,
+                     int32_t num_medusa_heads, int32_t* node_table, int32_t* n_nodes);
+
+/* Candidate tree from the Medusa heads (LMDeploy #1231 generate_candidates),
+ * laid out by a node table (tree_medusa_tree's, or any table of that
+ * layout whose parents precede their children).
+ *   node_table   HOST int32 [3][n_nodes] (parent, depth, rank rows).
  *   head_logits  device [B][num_medusa_heads][vocab] of head_dtype (TA_BF16
  *                or TA_F32); head h predicts the token at depth h + 1.
  *   root_token   device int32 [B]: the token decided by the previous step.
- * Nodes are numbered root 0, then the paths by length, then
- * lexicographically (node = 1 + position).  Writes, for every sequence:
- *   cand_tokens[b][n]  root_token[b] for n = 0; for the path (r_1..r_d) the
- *                      r_d-th best token of head d-1 (logit descending,
+ * Writes, for every sequence:
+ *   cand_tokens[b][n]  root_token[b] for n = 0; otherwise the rank[n]-th
+ *                      best token of head depth[n] - 1 (logit descending,
  *                      smaller token among equal logits, NaN ranks as -inf);
- *   tree_parent[b][n]  the node of (r_1..r_{d-1}) (-1 for the root);
- *   tree_depth[b][n]   d;
- * and padding (parent -2, depth 0, token 0) for n > n_choices up to t_max.
+ *   tree_parent[b][n]  parent[n];   tree_depth[b][n]  depth[n];
+ * and padding (parent -2, depth 0, token 0) for n_nodes <= n < t_max.
  * Uses batch, t_max and stream of desc.  topk <= 16 and <= vocab;
- * n_choices + 1 <= t_max.  An invalid list returns TA_ERR_CHOICES before
- * anything is enqueued; other errors as tree_vocab_argmax. */
-int tree_medusa_candidates(const tree_attn_desc* desc, const int32_t* choices, int32_t n_choices,
-                           int32_t max_len, const void* head_logits, int32_t head_dtype,
+ * n_nodes <= t_max.  The table is checked in O(n_nodes) (root -1/0, every
+ * parent earlier, depth = parent's + 1 <= num_medusa_heads, 0 <= rank <
+ * topk, siblings of distinct ranks): TA_ERR_CHOICES before anything is
+ * enqueued; other errors as tree_vocab_argmax. */
+int tree_medusa_candidates(const tree_attn_desc* desc, const int32_t* node_table,
+                           int32_t n_nodes, const void* head_logits, int32_t head_dtype,
                            int32_t num_medusa_heads, int32_t vocab, int32_t topk,
                            const int32_t* root_token, int32_t* cand_tokens, int32_t* tree_parent,
                            int32_t* tree_depth);

@@ -17,11 +17,18 @@ from ._lib import (  # noqa: F401
     kv_commit_path,
     load,
     make_desc,
+    tree_accept_commit,
     tree_accept_greedy,
+    tree_accept_typical,
+    tree_argmax_accept,
+    tree_attn_plan_info,
     tree_attn_rope_table,
     tree_attn_strerror,
     tree_attn_verify,
     tree_attn_workspace_init,
     tree_attn_workspace_size,
+    tree_medusa_candidates,
+    tree_medusa_tree,
+    tree_vocab_argmax,
 )
 from .runtime import TreeVerifier  # noqa: F401

@@ -36,7 +36,8 @@ STATUS = {
 }
 EXPORTED = (
     "tree_attn_verify", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
-    "tree_vocab_argmax", "tree_argmax_accept", "tree_medusa_candidates",
+    "tree_vocab_argmax", "tree_argmax_accept", "tree_accept_typical", "tree_medusa_tree",
+    "tree_medusa_candidates",
     "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_plan_info", "tree_attn_rope_table",
     "tree_attn_strerror",
 )
@@ -92,9 +93,14 @@ def load() -> ctypes.CDLL:
         "tree_accept_commit": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
         "tree_vocab_argmax": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P]),
         "tree_argmax_accept": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]),
-        "tree_medusa_candidates": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P,
+        "tree_accept_typical": (ctypes.c_int, [D, P, ctypes.c_int32, ctypes.c_int32, P, P,
+                                               ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                               P, P, P, P]),
+        "tree_medusa_tree": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, P, P]),
+        "tree_medusa_candidates": (ctypes.c_int, [D, P, ctypes.c_int32, P, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                  ctypes.c_int32, P, P, P, P]),
+                                                  P, P, P, P]),
         "tree_attn_workspace_size": (ctypes.c_size_t, [D]),
         "tree_attn_workspace_init": (ctypes.c_int, [D]),
         "tree_attn_plan_info": (ctypes.c_int, [D, P, P, P]),
@@ -270,6 +276,22 @@ def tree_argmax_accept(desc, logits, cand_tokens, tree_parent, node_argmax, acce
     _check(rc, "tree_argmax_accept")
 
 
+def tree_accept_typical(desc, logits, cand_tokens, tree_parent, node_stats, node_ok,
+                        accept_len, accept_path, temperature=1.0, epsilon=0.09, delta=0.3):
+    dt, V = _logits_args(desc, logits)
+    B, T = desc.batch, desc.t_max
+    for t, shp, name in ((cand_tokens, (B, T), "cand_tokens"), (tree_parent, (B, T), "tree_parent"),
+                         (node_ok, (B, T), "node_ok"), (accept_len, (B,), "accept_len"),
+                         (accept_path, (B, T), "accept_path")):
+        _expect(t, shp, torch.int32, name)
+    _expect(node_stats, (B, T, 2), torch.float32, "node_stats")
+    rc = load().tree_accept_typical(ctypes.byref(desc), _ptr(logits), dt, V, _ptr(cand_tokens),
+                                    _ptr(tree_parent), float(temperature), float(epsilon),
+                                    float(delta), _ptr(node_stats), _ptr(node_ok),
+                                    _ptr(accept_len), _ptr(accept_path))
+    _check(rc, "tree_accept_typical")
+
+
 def choices_array(choices):
     """A list of rank paths -> (int32 numpy [n][max_len] padded with -1)."""
     import numpy as np
@@ -281,9 +303,27 @@ def choices_array(choices):
     return a
 
 
-def tree_medusa_candidates(desc, choices, head_logits, topk, root_token, cand_tokens,
-                           tree_parent, tree_depth):
+def tree_medusa_tree(choices, topk, num_medusa_heads):
+    """A medusa choices list (paths of top-k ranks) -> its node table, int32
+    numpy [3][len(choices) + 1] (parent, depth, rank rows; root first, then
+    the paths by length, then lexicographically).  Host only: build it once
+    per list and pass it to every tree_medusa_candidates call."""
     import numpy as np
+    arr = np.ascontiguousarray(choices_array(choices))
+    n = len(choices)
+    table = np.zeros((3, n + 1), dtype=np.int32)
+    n_nodes = ctypes.c_int32(0)
+    rc = load().tree_medusa_tree(arr.ctypes.data_as(ctypes.c_void_p), n, arr.shape[1], int(topk),
+                                 int(num_medusa_heads), table.ctypes.data_as(ctypes.c_void_p),
+                                 ctypes.byref(n_nodes))
+    _check(rc, "tree_medusa_tree")
+    return table
+
+
+def tree_medusa_candidates(desc, node_table, head_logits, topk, root_token, cand_tokens,
+                           tree_parent, tree_depth):
+    """node_table: tree_medusa_tree's result (int32 numpy [3][n_nodes], C
+    order)."""
     B, T = desc.batch, desc.t_max
     if head_logits.dtype not in (torch.bfloat16, torch.float32) or head_logits.dim() != 3 \
             or head_logits.shape[0] != B:
@@ -293,12 +333,14 @@ def tree_medusa_candidates(desc, choices, head_logits, topk, root_token, cand_to
     for t, name in ((cand_tokens, "cand_tokens"), (tree_parent, "tree_parent"),
                     (tree_depth, "tree_depth")):
         _expect(t, (B, T), torch.int32, name)
-    arr = np.ascontiguousarray(choices_array(choices))
+    if node_table.dtype.name != "int32" or node_table.ndim != 2 or node_table.shape[0] != 3 \
+            or not node_table.flags["C_CONTIGUOUS"]:
+        raise TreeAttnError(-2, "node_table must be a C-contiguous int32 array [3][n_nodes]")
     rc = load().tree_medusa_candidates(
-        ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p), len(choices), arr.shape[1],
-        _ptr(head_logits), TA_BF16 if head_logits.dtype == torch.bfloat16 else TA_F32,
-        int(head_logits.shape[1]), int(head_logits.shape[2]), int(topk), _ptr(root_token),
-        _ptr(cand_tokens), _ptr(tree_parent), _ptr(tree_depth))
+        ctypes.byref(desc), node_table.ctypes.data, int(node_table.shape[1]), _ptr(head_logits),
+        TA_BF16 if head_logits.dtype == torch.bfloat16 else TA_F32, int(head_logits.shape[1]),
+        int(head_logits.shape[2]), int(topk), _ptr(root_token), _ptr(cand_tokens),
+        _ptr(tree_parent), _ptr(tree_depth))
     _check(rc, "tree_medusa_candidates")
 
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <vector>
 
@@ -243,24 +244,36 @@ int tree_argmax_accept(const tree_attn_desc* d, const void* logits, int32_t logi
   return status_of(e);
 }
 
-int tree_medusa_candidates(const tree_attn_desc* d, const int32_t* choices, int32_t n_choices,
-                           int32_t max_len, const void* head_logits, int32_t head_dtype,
-                           int32_t num_medusa_heads, int32_t vocab, int32_t topk,
-                           const int32_t* root_token, int32_t* cand_tokens, int32_t* tree_parent,
-                           int32_t* tree_depth) {
+int tree_accept_typical(const tree_attn_desc* d, const void* logits, int32_t logits_dtype,
+                        int32_t vocab, const int32_t* cand_tokens, const int32_t* tree_parent,
+                        float temperature, float epsilon, float delta, float* node_stats,
+                        int32_t* node_ok, int32_t* accept_len, int32_t* accept_path) {
   if (!d) return TA_ERR_NULL_POINTER;
   if (d->batch <= 0 || d->t_max <= 0 || d->batch > 65535) return TA_ERR_BAD_DIMS;
   if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
-  if (head_dtype != TA_BF16 && head_dtype != TA_F32) return TA_ERR_DTYPE;
-  if (!head_logits || !root_token || !cand_tokens || !tree_parent || !tree_depth ||
-      (n_choices > 0 && !choices))
-    return TA_ERR_NULL_POINTER;
-  if (num_medusa_heads <= 0 || num_medusa_heads > 65535 || vocab <= 0 || topk <= 0 ||
-      topk > kMaxTopK || topk > vocab || n_choices < 0 || max_len <= 0)
+  if (logits_dtype != TA_BF16 && logits_dtype != TA_F32) return TA_ERR_DTYPE;
+  if (vocab <= 0) return TA_ERR_BAD_DIMS;
+  if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(epsilon) ||
+      !std::isfinite(delta))
     return TA_ERR_BAD_DIMS;
-  if (n_choices + 1 > d->t_max) return TA_ERR_TREE_TOO_LARGE;
-  // Paths (host memory), validated and numbered: root 0, then by length,
-  // then lexicographically.
+  if (!logits || !cand_tokens || !tree_parent || !node_stats || !node_ok || !accept_len ||
+      !accept_path)
+    return TA_ERR_NULL_POINTER;
+  if ((reinterpret_cast<uintptr_t>(node_stats) & 7u) != 0) return TA_ERR_ALIGNMENT;
+  return status_of(launch_typical_accept(logits, logits_dtype, vocab, d->batch, d->t_max,
+                                         temperature, epsilon, delta, cand_tokens, tree_parent,
+                                         node_stats, node_ok, accept_len, accept_path,
+                                         static_cast<hipStream_t>(d->stream)));
+}
+
+int tree_medusa_tree(const int32_t* choices, int32_t n_choices, int32_t max_len, int32_t topk,
+                     int32_t num_medusa_heads, int32_t* node_table, int32_t* n_nodes) {
+  if (!node_table || !n_nodes || (n_choices > 0 && !choices)) return TA_ERR_NULL_POINTER;
+  if (num_medusa_heads <= 0 || topk <= 0 || topk > kMaxTopK || n_choices < 0 || max_len <= 0)
+    return TA_ERR_BAD_DIMS;
+  if (n_choices + 1 > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  // Paths, validated, then numbered: root 0, then by length, then
+  // lexicographically.
   std::vector<std::vector<int>> paths(n_choices);
   for (int c = 0; c < n_choices; ++c) {
     for (int j = 0; j < max_len; ++j) {
@@ -276,11 +289,11 @@ int tree_medusa_candidates(const tree_attn_desc* d, const int32_t* choices, int3
   std::sort(paths.begin(), paths.end(), [](const std::vector<int>& a, const std::vector<int>& b) {
     return a.size() != b.size() ? a.size() < b.size() : a < b;
   });
+  const int n = n_choices + 1;
+  std::vector<int32_t> table(3 * (size_t)n, 0);
   std::map<std::vector<int>, int> node_of;
   node_of[{}] = 0;
-  CandTree tree{};
-  tree.n_nodes = n_choices + 1;
-  tree.parent[0] = -1;
+  table[0] = -1;
   for (int c = 0; c < n_choices; ++c) {
     const std::vector<int>& p = paths[c];
     if (node_of.count(p)) return TA_ERR_CHOICES;  // duplicate
@@ -288,9 +301,49 @@ int tree_medusa_candidates(const tree_attn_desc* d, const int32_t* choices, int3
     const auto it = node_of.find(up);
     if (it == node_of.end()) return TA_ERR_CHOICES;  // prefix missing
     node_of[p] = c + 1;
-    tree.parent[c + 1] = (int8_t)it->second;
-    tree.depth[c + 1] = (int8_t)p.size();
-    tree.rank[c + 1] = (int8_t)p.back();
+    table[c + 1] = it->second;
+    table[n + c + 1] = (int32_t)p.size();
+    table[2 * n + c + 1] = p.back();
+  }
+  std::copy(table.begin(), table.end(), node_table);
+  *n_nodes = n;
+  return TA_OK;
+}
+
+int tree_medusa_candidates(const tree_attn_desc* d, const int32_t* node_table, int32_t n_nodes,
+                           const void* head_logits, int32_t head_dtype, int32_t num_medusa_heads,
+                           int32_t vocab, int32_t topk, const int32_t* root_token,
+                           int32_t* cand_tokens, int32_t* tree_parent, int32_t* tree_depth) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  if (d->batch <= 0 || d->t_max <= 0 || d->batch > 65535) return TA_ERR_BAD_DIMS;
+  if (d->t_max > kMaxTree) return TA_ERR_TREE_TOO_LARGE;
+  if (head_dtype != TA_BF16 && head_dtype != TA_F32) return TA_ERR_DTYPE;
+  if (!node_table || !head_logits || !root_token || !cand_tokens || !tree_parent || !tree_depth)
+    return TA_ERR_NULL_POINTER;
+  if (num_medusa_heads <= 0 || num_medusa_heads > 65535 || vocab <= 0 || topk <= 0 ||
+      topk > kMaxTopK || topk > vocab || n_nodes <= 0)
+    return TA_ERR_BAD_DIMS;
+  if (n_nodes > d->t_max) return TA_ERR_TREE_TOO_LARGE;
+  // O(n) check of the table: root first, parents before children, depth one
+  // below the parent's and within the heads, ranks below topk, no two
+  // children of a node with the same rank.
+  const int32_t* par = node_table;
+  const int32_t* dep = node_table + n_nodes;
+  const int32_t* rnk = node_table + 2 * (size_t)n_nodes;
+  if (par[0] != -1 || dep[0] != 0) return TA_ERR_CHOICES;
+  CandTree tree{};
+  tree.n_nodes = n_nodes;
+  tree.parent[0] = -1;
+  uint32_t used[kMaxTree] = {};
+  for (int n = 1; n < n_nodes; ++n) {
+    const int p = par[n];
+    if (p < 0 || p >= n || dep[n] != dep[p] + 1 || dep[n] > num_medusa_heads || rnk[n] < 0 ||
+        rnk[n] >= topk || (used[p] >> rnk[n]) & 1u)
+      return TA_ERR_CHOICES;
+    used[p] |= 1u << rnk[n];
+    tree.parent[n] = (int8_t)p;
+    tree.depth[n] = (int8_t)dep[n];
+    tree.rank[n] = (int8_t)rnk[n];
   }
   return status_of(launch_candidates(head_logits, head_dtype, vocab, num_medusa_heads, topk, tree,
                                      root_token, cand_tokens, tree_parent, tree_depth, d->batch,
@@ -320,7 +373,7 @@ const char* tree_attn_strerror(int status) {
     case TA_ERR_ROPE_TABLE: return "rope table missing or rope_max_pos < max_ctx_len + t_max";
     case TA_ERR_CAPACITY: return "max_blocks_per_seq * 16 < max_ctx_len";
     case TA_ERR_LAUNCH: return "kernel launch failed";
-    case TA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+    case TA_ERR_ALIGNMENT: return "a tensor pointer is not aligned as the call requires";
     case TA_ERR_CHOICES: return "the medusa choices list is not a valid tree";
     default: return "unknown status";
   }

@@ -8,10 +8,24 @@
 // token of every node at depth h + 1 (rank r of the node's path -> the r-th
 // best token).  No workgroup needs another's result, so one launch does it.
 //
-// Top-k: every thread keeps a sorted list of its best kMaxTopK values (larger
-// logit first, smaller token among equals; NaN ranks as -inf) while it
-// streams its share of the row with 16-byte loads; then k rounds of a
-// workgroup argmax over the list heads pick the winners in order.
+// Top-k without per-element sorting.  Every element (value, token) gets a
+// 64-bit key whose unsigned order is the top-k order: the value's bits made
+// monotone (NaN as -inf, -0 as +0) above the inverted token (smaller token
+// first among equal values); key 0 is below every element.  The row is
+// taken in segments of kSegChunks 16-byte chunks per thread, held in
+// registers; elements past the row's end read as -inf and are excluded by
+// index where -inf matters.  Per segment:
+//   1. each thread finds its best element: the max value, then the smallest
+//      token holding it;
+//   2. tau = the k-th best of the 256 thread bests.  The k threads whose best
+//      is at least tau hold k elements >= tau, so the segment's k best
+//      elements are all >= tau; no other thread holds anything >= tau;
+//   3. the elements >= tau (at most k * values per thread) and the k winners
+//      of the previous segment go to an LDS list;
+//   4. the list's k best are ranked by counting, for each entry, the entries
+//      above it (rounds of workgroup max when the list is long).
+// Typical rows put a few dozen elements on the list; the bound holds for any
+// data, ties and NaN included.
 #include "launch.h"
 #include "mfma_tile.h"
 
@@ -19,29 +33,52 @@ namespace ta {
 namespace {
 
 constexpr int kCandThreads = 256;
+constexpr int kSegChunks = 16;  // 16-byte chunks per thread per segment
 
-struct Entry {
-  float v;
-  int i;
-};
-
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+__device__ __forceinline__ uint64_t elem_key(float v, int i) {
+  uint32_t u = __float_as_uint(v != v ? -INFINITY : v);
+  u = u == 0x80000000u ? 0u : u;                  // -0 as +0
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // monotone in v
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)i;
 }
 
-// Insert (v, i) into the descending list L[0..kMaxTopK) (L[0] best).
-__device__ __forceinline__ void insert(Entry (&L)[kMaxTopK], float v, int i) {
-  v = v != v ? -INFINITY : v;  // NaN ranks as -inf
-  if (!better(v, i, L[kMaxTopK - 1].v, L[kMaxTopK - 1].i)) return;
-  Entry cur{v, i};
+__device__ __forceinline__ int key_token(uint64_t k) { return (int)~(uint32_t)k; }
+
+// Value j of a chunk.
+template <typename S>
+__device__ __forceinline__ float chunk_value(const u32x4& x, int j) {
+  if (sizeof(S) == 2) return (j & 1) ? bf16_hi(x[j >> 1]) : bf16_lo(x[j >> 1]);
+  return __uint_as_float(x[j]);
+}
+
+// Chunk c of a row (values c * kPer ...); values at or past V read as -inf.
+template <typename S>
+__device__ __forceinline__ u32x4 load_chunk(const S* row, int V, int c, bool vec) {
+  constexpr int kPer = 16 / sizeof(S);
+  constexpr uint32_t kNegInf = sizeof(S) == 2 ? 0xFF80FF80u : 0xFF800000u;
+  u32x4 x{kNegInf, kNegInf, kNegInf, kNegInf};
+  const int i0 = c * kPer;
+  if (i0 >= V) return x;
+  if (vec) return reinterpret_cast<const u32x4*>(row)[c];
+  if (sizeof(S) == 2) {
+    const uint16_t* r = reinterpret_cast<const uint16_t*>(row);
 #pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    if (better(cur.v, cur.i, L[s].v, L[s].i)) {
-      const Entry t = L[s];
-      L[s] = cur;
-      cur = t;
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = i0 + 2 * w < V ? r[i0 + 2 * w] : 0xFF80u;
+      const uint32_t hi = i0 + 2 * w + 1 < V ? r[i0 + 2 * w + 1] : 0xFF80u;
+      x[w] = lo | (hi << 16);
     }
+  } else {
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) x[w] = i0 + w < V ? r[i0 + w] : kNegInf;
   }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 template <typename S>
@@ -49,91 +86,134 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
     const S* __restrict__ head_logits, int V, int n_heads, int topk, CandTree tree,
     const int32_t* __restrict__ root_token, int32_t* __restrict__ cand,
     int32_t* __restrict__ parent, int32_t* __restrict__ depth, int T) {
-  __shared__ float s_v[kCandThreads / 64];
-  __shared__ int s_i[kCandThreads / 64];
-  __shared__ int s_top[kMaxTopK];
+  constexpr int kPer = 16 / sizeof(S);
+  constexpr int kSegValues = kSegChunks * kPer;           // per thread
+  constexpr int kCap = kMaxTopK * kSegValues + kMaxTopK;  // list bound
+  __shared__ __align__(16) uint64_t s_list[kCap];
+  __shared__ __align__(16) uint64_t s_best[kCandThreads];
+  __shared__ uint64_t s_red[kCandThreads / 64];
+  __shared__ uint64_t s_win[kMaxTopK];
+  __shared__ uint64_t s_tau;
+  __shared__ int s_n;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const S* row = head_logits + ((size_t)b * n_heads + h) * V;
-
-  Entry L[kMaxTopK];
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) L[s] = Entry{-INFINITY, 0x7FFFFFFF};
-  constexpr int kPer = 16 / sizeof(S);
   const bool vec = (V % kPer) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  if (vec) {
-    const int nchunks = V / kPer;
-    const u32x4* src = reinterpret_cast<const u32x4*>(row);
-    constexpr int kUnroll = 8;
-    for (int c0 = 0; c0 < nchunks; c0 += kUnroll * kCandThreads) {
-      u32x4 x[kUnroll];
+  const int nchunks = (V + kPer - 1) / kPer;
+
+  for (int c0 = 0, seg = 0; c0 < nchunks; c0 += kSegChunks * kCandThreads, ++seg) {
+    u32x4 x[kSegChunks];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kCandThreads + tid;
-        x[u] = c < nchunks ? src[c] : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int u = 0; u < kSegChunks; ++u)
+      x[u] = load_chunk(row, V, c0 + u * kCandThreads + tid, vec);
+    const int first = (c0 + tid) * kPer;  // this thread's smallest token here
+    // 1. this thread's best element
+    float m = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kCandThreads + tid;
-        if (c < nchunks) {
+    for (int u = 0; u < kSegChunks; ++u)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            if (sizeof(S) == 2) {
-              insert(L, bf16_lo(x[u][w]), c * kPer + 2 * w);
-              insert(L, bf16_hi(x[u][w]), c * kPer + 2 * w + 1);
-            } else {
-              insert(L, __uint_as_float(x[u][w]), c * kPer + w);
+      for (int j = 0; j < kPer; ++j) m = fmaxf(m, chunk_value<S>(x[u], j));  // NaN ignored
+    uint64_t best;
+    if (m > -INFINITY) {
+      int bi = 0;
+#pragma unroll
+      for (int u = kSegChunks - 1; u >= 0; --u)
+#pragma unroll
+        for (int j = kPer - 1; j >= 0; --j)
+          if (chunk_value<S>(x[u], j) == m) bi = (c0 + u * kCandThreads + tid) * kPer + j;
+      best = elem_key(m, bi);
+    } else {
+      // only -inf, NaN or nothing: all equal, the smallest token wins
+      best = first < V ? elem_key(-INFINITY, first) : 0ull;
+    }
+    s_best[tid] = best;
+    if (tid == 0) {
+      s_tau = 0ull;
+      s_n = 0;
+    }
+    __syncthreads();
+    // 2. tau: the thread best with exactly k - 1 above it (0 when fewer than
+    //    k threads have elements: then every element is listed)
+    int rank = 0;
+    const ulonglong2* sb = reinterpret_cast<const ulonglong2*>(s_best);
+#pragma unroll 8
+    for (int q = 0; q < kCandThreads / 2; ++q) {
+      const ulonglong2 e = sb[q];
+      rank += (e.x > best ? 1 : 0) + (e.y > best ? 1 : 0);
+    }
+    if (rank == topk - 1 && best != 0ull) s_tau = best;
+    __syncthreads();
+    // 3. the list: elements >= tau, then the previous segment's winners
+    const uint64_t tau = s_tau;
+    if (best >= tau) {  // this thread holds elements >= tau
+      const float tv = __uint_as_float((uint32_t)(tau >> 32) & 0x80000000u
+                                           ? (uint32_t)(tau >> 32) & 0x7FFFFFFFu
+                                           : ~(uint32_t)(tau >> 32));
+      const bool exact = !(tv > -INFINITY);  // tau is -inf or none: test keys
+#pragma unroll
+      for (int u = 0; u < kSegChunks; ++u) {
+        const int i0 = (c0 + u * kCandThreads + tid) * kPer;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const float v = chunk_value<S>(x[u], j);
+          if (exact || v >= tv) {
+            const uint64_t k = elem_key(v, i0 + j);
+            if (i0 + j < V && k >= tau) {
+              const int slot = atomicAdd(&s_n, 1);
+              if (slot < kCap) s_list[slot] = k;
             }
           }
         }
       }
     }
-  } else {
-    for (int i = tid; i < V; i += kCandThreads) insert(L, ld(row, i), i);
-  }
-
-  // k rounds: the best list head of the workgroup is the next token.
-  for (int r = 0; r < topk; ++r) {
-    float v = L[0].v;
-    int i = L[0].i;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(v, off);
-      const int oi = __shfl_xor(i, off);
-      if (better(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-      }
-    }
-    if (lane == 0) {
-      s_v[wv] = v;
-      s_i[wv] = i;
+    if (seg > 0 && tid < topk) {
+      const int slot = atomicAdd(&s_n, 1);
+      if (slot < kCap) s_list[slot] = s_win[tid];
     }
     __syncthreads();
-    float bv = s_v[0];
-    int bi = s_i[0];
-#pragma unroll
-    for (int w = 1; w < kCandThreads / 64; ++w)
-      if (better(s_v[w], s_i[w], bv, bi)) {
-        bv = s_v[w];
-        bi = s_i[w];
+    // 4. the list's k best, in order
+    const int n = min(s_n, kCap);
+    if (n <= kCandThreads) {
+      if (tid < n) {
+        const uint64_t e = s_list[tid];
+        int r = (n & 1) && s_list[n - 1] > e ? 1 : 0;
+        const ulonglong2* sl = reinterpret_cast<const ulonglong2*>(s_list);
+        for (int q = 0; q < n / 2; ++q) {
+          const ulonglong2 p = sl[q];
+          r += (p.x > e ? 1 : 0) + (p.y > e ? 1 : 0);
+        }
+        if (r < topk) s_win[r] = e;
       }
-    if (tid == 0) s_top[r] = bi;
-    if (L[0].i == bi && L[0].v == bv) {  // this thread's head won: drop it
+      __syncthreads();
+    } else {
+      uint64_t prev = ~0ull;  // above every element
+      for (int r = 0; r < topk; ++r) {
+        uint64_t w = 0ull;
+        for (int q = tid; q < n; q += kCandThreads) {
+          const uint64_t e = s_list[q];
+          if (e < prev && e > w) w = e;
+        }
 #pragma unroll
-      for (int s = 0; s + 1 < kMaxTopK; ++s) L[s] = L[s + 1];
-      L[kMaxTopK - 1] = Entry{-INFINITY, 0x7FFFFFFF};
+        for (int off = 32; off > 0; off >>= 1) {
+          const uint64_t o = shfl_xor_u64(w, off);
+          w = o > w ? o : w;
+        }
+        if (lane == 0) s_red[wv] = w;
+        __syncthreads();
+        w = s_red[0];
+#pragma unroll
+        for (int q = 1; q < kCandThreads / 64; ++q) w = s_red[q] > w ? s_red[q] : w;
+        if (tid == 0) s_win[r] = w;
+        prev = w;
+        __syncthreads();
+      }
     }
-    __syncthreads();
   }
 
   // Nodes at depth h + 1 take their rank's token.
   const size_t base = (size_t)b * T;
   for (int n = tid; n < tree.n_nodes; n += kCandThreads) {
-    if (n > 0 && tree.depth[n] == h + 1) {
-      const int tok = s_top[tree.rank[n]];
-      cand[base + n] = tok < V ? tok : 0;  // V < k: missing ranks give token 0
-    }
+    if (n > 0 && tree.depth[n] == h + 1) cand[base + n] = key_token(s_win[tree.rank[n]]);
   }
   if (h == 0) {
     for (int n = tid; n < T; n += kCandThreads) {

@@ -108,17 +108,21 @@ __global__ __launch_bounds__(kArgThreads) void vocab_argmax_kernel(const S* __re
 // p = softmax(logits / temperature) after node n and H its entropy, child c
 // of n passes iff p[cand_tokens[c]] > min(epsilon, delta * exp(-H)).
 //
-// Kernel 1, one workgroup per (sequence, node) row: a single pass over the
-// row keeps, per thread and then merged over the workgroup, the running max
-// m of y = x / temperature, z = sum e^(y - m) and s = sum e^(y - m) (y - m)
-// (rescaled by e^(m - m') when the max moves to m'); then
-// lse = m + ln z and H = ln z - s / z.  Kernel 2, one wavefront per
-// sequence: each child gathers its token's logit from the parent's row and
-// tests p = e^(x / temperature - lse) against the threshold; the path is then
-// chosen as in greedy acceptance.
+// Kernel 1, one workgroup per (sequence, node) row, one pass over the row in
+// base 2: with u = x * log2(e) / temperature, every thread keeps the running
+// max m of u, z = sum 2^(u - m) and s = sum 2^(u - m) (u - m).  Each batch
+// of up to 16 x 16 bytes per thread is held in registers, so its max is
+// taken first and the batch adds to (m, z, s) with one rescale
+// (2^(m - m') when the max moves to m').  Since e^(y - M) = 2^(u - m) and
+// y - M = (u - m) ln 2 for y = x / temperature and its max M,
+//   lse = (m + log2 z) ln 2,   H = ln z - sum e^(y - M) (y - M) / z
+//                                = (log2 z - s / z) ln 2.
+// Kernel 2, one wavefront per sequence: each child gathers its token's logit
+// from the parent's row and tests p = e^(x / temperature - lse) against the
+// threshold; the path is then chosen as in greedy acceptance.
 // ---------------------------------------------------------------------------
 struct Lse {
-  float m, z, s;
+  float m, z, s;  // base-2 running max, sum of 2^(u - m), sum of 2^(u - m) (u - m)
 };
 
 // Merge b into a (both over disjoint sets of values).
@@ -129,39 +133,31 @@ __device__ __forceinline__ void merge_lse(Lse& a, const Lse& b) {
     return;
   }
   if (b.m > a.m) {
-    const float f = __expf(a.m - b.m);
-    a.s = f * (a.s + (a.m - b.m) * a.z) + b.s;
+    const float d = a.m - b.m, f = __builtin_amdgcn_exp2f(d);
+    a.s = f * (a.s + d * a.z) + b.s;
     a.z = f * a.z + b.z;
     a.m = b.m;
   } else {
-    const float f = __expf(b.m - a.m);
-    a.s += f * (b.s + (b.m - a.m) * b.z);
+    const float d = b.m - a.m, f = __builtin_amdgcn_exp2f(d);
+    a.s += f * (b.s + d * b.z);
     a.z += f * b.z;
   }
 }
 
-template <int kN>
-__device__ __forceinline__ void add_values(Lse& a, const float (&y)[kN], int n) {
-  float mt = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kN; ++j)
-    if (j < n) mt = fmaxf(mt, y[j]);
-  if (mt == -INFINITY) return;  // nothing but -inf: no mass
-  Lse t{mt, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kN; ++j)
-    if (j < n) {
-      const float d = y[j] - mt;
-      const float e = __expf(d);
-      t.z += e;
-      t.s += d == -INFINITY ? 0.f : e * d;
-    }
-  merge_lse(a, t);
+// Adds 2^(u - m) and its weighted term for one value u = x * c, relative to
+// the batch max m.  Values far below m (and -inf) add nothing: the
+// difference is clamped where 2^d is already 0 in fp32, which also keeps
+// 0 * (-inf) out of s.
+__device__ __forceinline__ void add_term(Lse& t, float x, float c) {
+  const float d = fmaxf(fmaf(x, c, -t.m), -256.f);
+  const float e = __builtin_amdgcn_exp2f(d);
+  t.z += e;
+  t.s = fmaf(e, d, t.s);
 }
 
 template <typename S>
 __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __restrict__ logits,
-                                                                  int V, float inv_temp,
+                                                                  int V, float c,
                                                                   float2* __restrict__ stats) {
   __shared__ Lse s_l[kArgThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -177,29 +173,45 @@ __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __res
       u32x4 x[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kArgThreads + tid;
-        x[u] = c < nchunks ? src[c] : u32x4{0u, 0u, 0u, 0u};
+        const int ch = c0 + u * kArgThreads + tid;
+        x[u] = ch < nchunks ? src[ch] : u32x4{0u, 0u, 0u, 0u};
       }
+      // Batch max of the raw values (c > 0, so it is also the max of u).
+      float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kArgThreads + tid;
-        float y[kPer];
+        if (c0 + u * kArgThreads + tid < nchunks) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if (sizeof(S) == 2) {
-            y[2 * w] = bf16_lo(x[u][w]) * inv_temp;
-            y[2 * w + 1] = bf16_hi(x[u][w]) * inv_temp;
-          } else {
-            y[w] = __uint_as_float(x[u][w]) * inv_temp;
+          for (int w = 0; w < 4; ++w)
+            mx = sizeof(S) == 2 ? fmaxf(mx, fmaxf(bf16_lo(x[u][w]), bf16_hi(x[u][w])))
+                                : fmaxf(mx, __uint_as_float(x[u][w]));
+        }
+      }
+      if (mx == -INFINITY) continue;  // nothing but -inf (or no values): no mass
+      Lse t{mx * c, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (c0 + u * kArgThreads + tid < nchunks) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if (sizeof(S) == 2) {
+              add_term(t, bf16_lo(x[u][w]), c);
+              add_term(t, bf16_hi(x[u][w]), c);
+            } else {
+              add_term(t, __uint_as_float(x[u][w]), c);
+            }
           }
         }
-        add_values(a, y, c < nchunks ? kPer : 0);
       }
+      merge_lse(a, t);
     }
   } else {
     for (int i = tid; i < V; i += kArgThreads) {
-      const float y[1] = {ld(row, i) * inv_temp};
-      add_values(a, y, 1);
+      const float x = ld(row, i);
+      if (x == -INFINITY) continue;
+      Lse t{x * c, 0.f, 0.f};
+      add_term(t, x, c);
+      merge_lse(a, t);
     }
   }
 #pragma unroll
@@ -213,8 +225,9 @@ __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __res
     Lse r = s_l[0];
 #pragma unroll
     for (int w = 1; w < kArgThreads / 64; ++w) merge_lse(r, s_l[w]);
-    const float lz = __logf(r.z);
-    stats[blockIdx.x] = r.z > 0.f ? float2{r.m + lz, lz - r.s / r.z}
+    constexpr float kLn2 = 0.69314718055994531f;
+    const float l2z = __log2f(r.z);
+    stats[blockIdx.x] = r.z > 0.f ? float2{(r.m + l2z) * kLn2, (l2z - r.s / r.z) * kLn2}
                                   : float2{-INFINITY, __builtin_nanf("")};
   }
 }
@@ -253,16 +266,17 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int V, int B, in
                                  float* node_stats, int32_t* node_ok, int32_t* accept_len,
                                  int32_t* accept_path, hipStream_t stream) {
   const float inv_temp = 1.0f / temperature;
+  const float c = 1.4426950408889634f / temperature;  // log2(e) / temperature
   float2* stats = reinterpret_cast<float2*>(node_stats);
   if (dtype == TA_BF16) {
     hipLaunchKernelGGL(row_entropy_kernel<uint16_t>, dim3((unsigned)(B * T)), dim3(kArgThreads),
-                       0, stream, static_cast<const uint16_t*>(logits), V, inv_temp, stats);
+                       0, stream, static_cast<const uint16_t*>(logits), V, c, stats);
     hipLaunchKernelGGL(typical_accept_kernel<uint16_t>, dim3((unsigned)B), dim3(64), 0, stream,
                        static_cast<const uint16_t*>(logits), V, T, inv_temp, epsilon, delta,
                        stats, cand_tokens, tree_parent, node_ok, accept_len, accept_path);
   } else {
     hipLaunchKernelGGL(row_entropy_kernel<float>, dim3((unsigned)(B * T)), dim3(kArgThreads), 0,
-                       stream, static_cast<const float*>(logits), V, inv_temp, stats);
+                       stream, static_cast<const float*>(logits), V, c, stats);
     hipLaunchKernelGGL(typical_accept_kernel<float>, dim3((unsigned)B), dim3(64), 0, stream,
                        static_cast<const float*>(logits), V, T, inv_temp, epsilon, delta,
                        stats, cand_tokens, tree_parent, node_ok, accept_len, accept_path);

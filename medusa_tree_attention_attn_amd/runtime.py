@@ -14,7 +14,8 @@ import torch
 
 from . import _lib
 from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_commit,
-                   tree_accept_greedy, tree_argmax_accept, tree_medusa_candidates,
+                   tree_accept_greedy, tree_accept_typical, tree_argmax_accept,
+                   tree_medusa_candidates, tree_medusa_tree,
                    tree_vocab_argmax,
                    tree_attn_rope_table, tree_attn_verify, tree_attn_workspace_init,
                    tree_attn_workspace_size)
@@ -114,11 +115,41 @@ class TreeVerifier:
                            accept_path)
         return node_argmax, accept_len, accept_path
 
+    def accept_typical(self, logits, cand_tokens, tree_parent, temperature=1.0, epsilon=0.09,
+                       delta=0.3, node_stats=None, node_ok=None, accept_len=None,
+                       accept_path=None):
+        """Typical acceptance: a child passes when its token's probability
+        under softmax(logits / temperature) at the parent exceeds
+        min(epsilon, delta * exp(-entropy)).  Returns (node_stats [B][T][2] =
+        (log-sum-exp, entropy), node_ok, accept_len, accept_path)."""
+        self._sync_stream()
+        B, T = self.desc.batch, self.desc.t_max
+        if node_stats is None:
+            node_stats = torch.empty((B, T, 2), dtype=torch.float32, device=self.device)
+        if node_ok is None:
+            node_ok = torch.empty((B, T), dtype=torch.int32, device=self.device)
+        if accept_len is None:
+            accept_len = torch.empty((B,), dtype=torch.int32, device=self.device)
+        if accept_path is None:
+            accept_path = torch.empty((B, T), dtype=torch.int32, device=self.device)
+        tree_accept_typical(self.desc, logits, cand_tokens, tree_parent, node_stats, node_ok,
+                            accept_len, accept_path, temperature, epsilon, delta)
+        return node_stats, node_ok, accept_len, accept_path
+
+    @staticmethod
+    def medusa_tree(choices, topk, num_medusa_heads):
+        """Node table of a medusa choices list, built once on the host."""
+        return tree_medusa_tree(choices, topk, num_medusa_heads)
+
     def candidates(self, choices, head_logits, topk, root_token, cand_tokens=None,
                    tree_parent=None, tree_depth=None):
         """Candidate tree from Medusa head logits [B][heads][vocab] laid out by a
-        medusa-choices list (paths of top-k ranks); returns (cand_tokens,
+        medusa-choices list: either the list itself (paths of top-k ranks,
+        numbered on every call) or its node table from medusa_tree() (the
+        fast path for a list used every step).  Returns (cand_tokens,
         tree_parent, tree_depth)."""
+        if not hasattr(choices, "ctypes"):
+            choices = tree_medusa_tree(choices, topk, head_logits.shape[1])
         self._sync_stream()
         B, T = self.desc.batch, self.desc.t_max
         mk = lambda: torch.empty((B, T), dtype=torch.int32, device=self.device)

@@ -157,33 +157,109 @@ def test_argmax_entry_checks(lib):
     assert lib.tree_argmax_accept(d, *bad) == -2
 
 
-def _cand_rc(lib, choices, topk=10, heads=4, vocab=32000, t_max=64, n=None):
+def test_typical_entry_checks(lib):
+    d = ctypes.byref(_desc())
+    # logits, dtype, vocab, cand, parent, temperature, epsilon, delta, stats, ok, len, path
+    args = [0x3000, 0, 32000, 0x4000, 0x4100, 1.0, 0.09, 0.3, 0x4200, 0x4300, 0x4400, 0x4500]
+    assert lib.tree_accept_typical(None, *args) == -1
+    for which in (0, 3, 4, 8, 9, 10, 11):
+        bad = list(args)
+        bad[which] = None
+        assert lib.tree_accept_typical(d, *bad) == -1
+    for which, value, code in ((1, 5, -3), (2, 0, -2), (5, 0.0, -2), (5, -1.0, -2),
+                               (5, float("inf"), -2), (6, float("nan"), -2),
+                               (7, float("inf"), -2), (8, 0x4204, -12)):
+        bad = list(args)
+        bad[which] = value
+        assert lib.tree_accept_typical(d, *bad) == code, (which, value)
+    assert lib.tree_accept_typical(ctypes.byref(_desc(t_max=65)), *args) == -4
+    assert lib.tree_accept_typical(ctypes.byref(_desc(batch=0)), *args) == -2
+
+
+def _tree_rc(lib, choices, topk=10, heads=4, n=None):
     import numpy as np
     from medusa_tree_attention_attn_amd._lib import choices_array
     arr = np.ascontiguousarray(choices_array(choices))
-    return lib.tree_medusa_candidates(
-        ctypes.byref(_desc(t_max=t_max)), arr.ctypes.data_as(ctypes.c_void_p),
-        len(choices) if n is None else n, arr.shape[1], 0x3000, 0, heads, vocab, topk,
-        0x4000, 0x5000, 0x6000, 0x7000)
+    table = np.full((3, 65), 77, dtype=np.int32)
+    nn = ctypes.c_int32(-5)
+    rc = lib.tree_medusa_tree(arr.ctypes.data_as(ctypes.c_void_p),
+                              len(choices) if n is None else n, arr.shape[1], topk, heads,
+                              table.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nn))
+    return rc, table, nn.value
 
 
 def test_medusa_choices_validated_on_host(lib):
-    """Every rejection happens before anything is enqueued (no device here)."""
-    assert _cand_rc(lib, [(0,), (0,)]) == -13                  # duplicate path
-    assert _cand_rc(lib, [(0,), (1, 0)]) == -13                # prefix (1,) missing
-    assert _cand_rc(lib, [(0,), (10,)]) == -13                 # rank >= topk
-    assert _cand_rc(lib, [(0,), (0, 0), (0, 0, 0), (0, 0, 0, 0), (0, 0, 0, 0, 0)]) == -13  # deeper than 4 heads
-    assert _cand_rc(lib, [(0,), (0, 0)], t_max=2) == -4       # 3 nodes > t_max
-    assert _cand_rc(lib, [(0,)], topk=17) == -2                # topk > 16
-    assert _cand_rc(lib, [(0,)], topk=8, vocab=7) == -2        # topk > vocab
+    """Every rejection happens on the host; outputs stay untouched."""
+    for choices, kw, code in (
+            ([(0,), (0,)], {}, -13),                            # duplicate path
+            ([(0,), (1, 0)], {}, -13),                          # prefix (1,) missing
+            ([(0,), (10,)], {}, -13),                           # rank >= topk
+            ([(0,), (0, 0), (0, 0, 0), (0, 0, 0, 0), (0, 0, 0, 0, 0)], {}, -13),  # > 4 heads
+            ([(0,)], dict(topk=17), -2),                        # topk > 16
+            ([(0,)], dict(heads=0), -2),
+            ([(i,) for i in range(8)] + [(i, j) for i in range(8) for j in range(8)],
+             dict(topk=8), -4)):                                # 73 nodes > 64
+        rc, table, nn = _tree_rc(lib, choices, **kw)
+        assert rc == code, choices
+        assert nn == -5 and (table == 77).all()
     import numpy as np
     gap = np.array([[0, -1, 1]], dtype=np.int32)               # -1 then a rank
-    assert lib.tree_medusa_candidates(ctypes.byref(_desc()), gap.ctypes.data_as(ctypes.c_void_p),
-                                      1, 3, 0x3000, 0, 4, 100, 4, 0x4000, 0x5000, 0x6000,
-                                      0x7000) == -13
-    assert lib.tree_medusa_candidates(ctypes.byref(_desc()), None, 1, 1, 0x3000, 0, 4, 100, 4,
+    out = np.zeros((3, 2), dtype=np.int32)
+    nn = ctypes.c_int32(0)
+    assert lib.tree_medusa_tree(gap.ctypes.data_as(ctypes.c_void_p), 1, 3, 4, 4,
+                                out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(nn)) == -13
+    assert lib.tree_medusa_tree(None, 1, 1, 4, 4, out.ctypes.data_as(ctypes.c_void_p),
+                                ctypes.byref(nn)) == -1
+
+
+def test_medusa_tree_numbering_matches_oracle(lib):
+    """The library's node numbering is the oracle's (root, then paths by
+    length, then lexicographically), on lists given in shuffled order."""
+    import numpy as np
+    from oracle.candidates import choice_tree
+    from synth import make_choices
+    for seed, n, depth, k in ((0, 63, 4, 10), (1, 20, 5, 3), (2, 1, 1, 1), (3, 40, 2, 16)):
+        choices = make_choices(seed, n=n, max_depth=depth, topk=k)
+        order = np.random.default_rng(seed).permutation(len(choices))
+        shuffled = [choices[i] for i in order]
+        rc, table, nn = _tree_rc(lib, shuffled, topk=k, heads=depth)
+        assert rc == 0 and nn == n + 1
+        paths, parent, dep = choice_tree(choices)
+        flat = table.reshape(-1)[:3 * nn].reshape(3, nn)   # the call writes [3][n_nodes]
+        assert np.array_equal(flat[0], parent) and np.array_equal(flat[1], dep)
+        assert flat[2].tolist() == [0] + [p[-1] for p in paths]
+    rc, table, nn = _tree_rc(lib, [], topk=4)
+    assert rc == 0 and nn == 1 and table.reshape(-1)[:3].tolist() == [-1, 0, 0]
+
+
+def _cand_rc(lib, table, topk=10, heads=4, vocab=32000, t_max=64):
+    import numpy as np
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    return lib.tree_medusa_candidates(
+        ctypes.byref(_desc(t_max=t_max)), table.ctypes.data_as(ctypes.c_void_p), table.shape[1],
+        0x3000, 0, heads, vocab, topk, 0x4000, 0x5000, 0x6000, 0x7000)
+
+
+def test_medusa_candidates_checks_the_table(lib):
+    """Every rejection happens before anything is enqueued (no device here)."""
+    # parent, depth, rank rows of root -> (0,) -> (0, 0)
+    good = [[-1, 0, 1], [0, 1, 2], [0, 0, 0]]
+    for bad in ([[0, 0, 1], [0, 1, 2], [0, 0, 0]],          # root with a parent
+                [[-1, 0, 1], [1, 1, 2], [0, 0, 0]],         # root depth != 0
+                [[-1, 2, 1], [0, 1, 2], [0, 0, 0]],         # parent after the child
+                [[-1, 0, 1], [0, 1, 3], [0, 0, 0]],         # depth != parent's + 1
+                [[-1, 0, 1], [0, 1, 2], [0, 10, 0]],        # rank >= topk
+                [[-1, 0, 1], [0, 1, 2], [0, -1, 0]],        # negative rank
+                [[-1, 0, 0], [0, 1, 1], [0, 3, 3]]):        # two siblings of one rank
+        assert _cand_rc(lib, bad) == -13, bad
+    chain = [[-1, 0, 1, 2, 3, 4], [0, 1, 2, 3, 4, 5], [0] * 6]
+    assert _cand_rc(lib, chain) == -13                       # deeper than 4 heads
+    assert _cand_rc(lib, good, t_max=2) == -4                # 3 nodes > t_max
+    assert _cand_rc(lib, good, topk=17) == -2                # topk > 16
+    assert _cand_rc(lib, good, topk=8, vocab=7) == -2        # topk > vocab
+    assert _cand_rc(lib, good, heads=0) == -2
+    assert lib.tree_medusa_candidates(ctypes.byref(_desc()), None, 3, 0x3000, 0, 4, 100, 4,
                                       0x4000, 0x5000, 0x6000, 0x7000) == -1
-    assert _cand_rc(lib, [(0,)], heads=0) == -2
 
 
 def test_plan_info_follows_flags(lib):

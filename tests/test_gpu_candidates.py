@@ -21,6 +21,8 @@ pytestmark = pytest.mark.gpu
     (2, 2, 12, 12, 10, 2, torch.float32, 4, 4),          # topk == vocab
     (5, 1, 500, 3, 3, 1, torch.bfloat16, 1, 5),          # one head, a root with 3 children
     (1, 4, 32000, 10, 0, 4, torch.bfloat16, 0, 6),       # no choices: root only
+    (2, 2, 100000, 10, 20, 2, torch.bfloat16, 1, 8),     # several segments per row
+    (2, 3, 150001, 16, 30, 3, torch.bfloat16, 2, 7),     # several segments, scalar path
 ])
 def test_candidates_bit_exact(B, H, V, topk, n, depth, dtype, ties, seed):
     choices = make_choices(seed, n=n, max_depth=depth, topk=topk) if n else []
@@ -58,3 +60,50 @@ def test_candidate_tree_drives_verify_and_accept():
     assert np.abs(out.float().cpu().numpy() - ref).max() <= 1e-2
     Lr, Pathr = oracle.accept_greedy(wl.node_argmax, Cr, Pr)
     assert np.array_equal(L.cpu().numpy(), Lr) and np.array_equal(path.cpu().numpy(), Pathr)
+
+
+def test_prepared_table_reused_across_calls():
+    """A node table built once drives repeated calls on new head logits;
+    each call equals the oracle's assembly (and the list form's output)."""
+    B, H, V, topk = 4, 4, 32000, 10
+    choices = make_choices(11, n=63, max_depth=4, topk=topk)
+    wl = make_workload("vicuna7b_b16", 11, batch=B, heads=1, ctx_range=(16, 16))
+    tv = verifier(wl)
+    table = tv.medusa_tree(choices, topk, H)
+    for rep in range(3):
+        logits = make_head_logits(B, H, V, seed=100 + rep, ties=rep)
+        root = torch.arange(B, dtype=torch.int32) + rep
+        C, P, D = tv.candidates(table, logits.cuda(), topk, root.cuda())
+        C2, P2, D2 = tv.candidates(choices, logits.cuda(), topk, root.cuda())
+        torch.cuda.synchronize()
+        Cr, Pr, Dr = assemble_candidates(logits, choices, root.numpy(), wl.spec.t_max, topk)
+        assert np.array_equal(C.cpu().numpy(), Cr), rep
+        assert np.array_equal(P.cpu().numpy(), Pr) and np.array_equal(D.cpu().numpy(), Dr)
+        assert torch.equal(C, C2) and torch.equal(P, P2) and torch.equal(D, D2)
+
+
+def test_candidates_adversarial_rows():
+    """Rows whose best values all sit in a few threads' share of the row (a
+    long candidate list: the rounds path), all-equal rows (ties decided by
+    token), rows of -inf and NaN, and a +inf."""
+    B, H, V, topk = 1, 4, 32000, 16
+    choices = make_choices(9, n=60, max_depth=4, topk=topk)
+    x = make_head_logits(B, H, V, seed=9, dtype=torch.float32)
+    idx = torch.arange(V)
+    chunk = idx // 8                                      # 16-byte bf16 chunks
+    crowd = (chunk % 256) < 3                             # three threads' share
+    x[0, 0] = torch.where(crowd, 100.0 + (idx % 97).float() / 8, x[0, 0])
+    x[0, 1] = 1.5                                         # all equal
+    x[0, 2] = -float("inf")
+    x[0, 2, 31999] = float("nan")
+    x[0, 2, 7] = float("inf")
+    x[0, 3, ::3] = float("nan")
+    logits = x.to(torch.bfloat16)
+    root = torch.tensor([4], dtype=torch.int32)
+    wl = make_workload("vicuna7b_b16", 9, batch=B, heads=1, ctx_range=(16, 16))
+    tv = verifier(wl)
+    C, P, D = tv.candidates(choices, logits.cuda(), topk, root.cuda())
+    torch.cuda.synchronize()
+    Cr, Pr, Dr = assemble_candidates(logits, choices, root.numpy(), wl.spec.t_max, topk)
+    assert np.array_equal(C.cpu().numpy(), Cr)
+    assert np.array_equal(P.cpu().numpy(), Pr) and np.array_equal(D.cpu().numpy(), Dr)
