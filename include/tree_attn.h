@@ -80,7 +80,8 @@ enum ta_flags {
   TA_FLAG_GRID_KERNEL = 2,    /* MFMA verify: one workgroup per work item      */
   TA_FLAG_PERSISTENT_KERNEL = 4 /* MFMA verify: one resident workgroup per CU   */
                               /* taking work items from a counter.  Without    */
-                              /* either flag the library takes the persistent  */
+                              /* either flag the library takes the decode      */
+                              /* kernel when t_max == 1, else the persistent   */
                               /* kernel when there are at least 4 work items   */
                               /* per CU, else the grid kernel.                 */
 };
@@ -284,17 +285,25 @@ int tree_medusa_candidates(const tree_attn_desc* desc, const int32_t* node_table
                            int32_t* tree_depth);
 
 /* Bytes of workspace tree_attn_verify needs for this descriptor (0 if the
- * descriptor is invalid or takes the plain kernel): for the MFMA kernels,
- * 256 bytes of work counters plus split-KV partials when the plan splits
- * contexts.  Pure host computation. */
+ * descriptor is invalid or takes the plain or the decode kernel): for the
+ * MFMA kernels, 256 bytes of work counters plus split-KV partials when the
+ * plan splits contexts.  Pure host computation. */
 size_t tree_attn_workspace_size(const tree_attn_desc* desc);
 
 /* Kernels tree_attn_verify launches for this descriptor on the current
- * device: *kernel = TA_KERNEL_SIMPLE, TA_KERNEL_GRID or TA_KERNEL_PERSISTENT;
- * *splits = context splits per (sequence, head) (a merge kernel follows when
- * it is > 1); *split_tokens = context tokens per split.  Output pointers may
- * be NULL.  Host-only query; errors as tree_attn_verify's descriptor checks. */
-enum ta_kernel { TA_KERNEL_SIMPLE = 0, TA_KERNEL_GRID = 1, TA_KERNEL_PERSISTENT = 2 };
+ * device: *kernel = TA_KERNEL_SIMPLE, TA_KERNEL_GRID, TA_KERNEL_PERSISTENT or
+ * TA_KERNEL_DECODE (t_max == 1 with bf16 and head_dim 128 and neither MFMA
+ * flag: one workgroup per (sequence, head) streams its whole context, no
+ * splits, no workspace); *splits = context splits per (sequence, head) (a
+ * merge kernel follows when it is > 1); *split_tokens = context tokens per
+ * split.  Output pointers may be NULL.  Host-only query; errors as
+ * tree_attn_verify's descriptor checks. */
+enum ta_kernel {
+  TA_KERNEL_SIMPLE = 0,
+  TA_KERNEL_GRID = 1,
+  TA_KERNEL_PERSISTENT = 2,
+  TA_KERNEL_DECODE = 3
+};
 int tree_attn_plan_info(const tree_attn_desc* desc, int32_t* kernel, int32_t* splits,
                         int32_t* split_tokens);
 

@@ -344,7 +344,8 @@ def tree_medusa_candidates(desc, node_table, head_logits, topk, root_token, cand
     _check(rc, "tree_medusa_candidates")
 
 
-KERNEL_NAMES = {0: "verify_simple_kernel", 1: "verify_mfma_kernel", 2: "verify_stream_kernel"}
+KERNEL_NAMES = {0: "verify_simple_kernel", 1: "verify_mfma_kernel", 2: "verify_stream_kernel",
+                3: "verify_decode_kernel"}
 
 
 def tree_attn_plan_info(desc):

@@ -60,7 +60,9 @@ int tree_attn_plan_info(const tree_attn_desc* d, int32_t* kernel, int32_t* split
   if (rc != TA_OK) return rc;
   const Plan plan = make_plan(*d);
   int k = TA_KERNEL_SIMPLE;
-  if (plan.mfma) {
+  if (plan.decode) {
+    k = TA_KERNEL_DECODE;
+  } else if (plan.mfma) {
     const long long items = (long long)d->batch * d->num_heads * plan.splits;
     k = use_stream_kernel(*d, items, device_cu_count()) ? TA_KERNEL_PERSISTENT : TA_KERNEL_GRID;
   }
@@ -121,6 +123,7 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   hipStream_t stream = static_cast<hipStream_t>(d->stream);
   const int n_cu = device_cu_count();
   p.n_cu = n_cu;
+  if (plan.decode) return status_of(launch_verify_decode(p, stream));
   if (plan.mfma) {
     char* ws = static_cast<char*>(d->workspace);
     if (plan.splits > 1) {

@@ -17,6 +17,8 @@ hipError_t launch_verify_simple(const VerifyParams& p, int dtype, hipStream_t st
 // counters at p.ws_ctr).  When a context can take more than one split, the
 // split partials are merged by launch_split_combine afterwards.
 hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream);
+// One-node trees (T = 1): one workgroup per (sequence, head), no workspace.
+hipError_t launch_verify_decode(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_verify_stream(const VerifyParams& p, hipStream_t stream);
 hipError_t launch_split_combine(const VerifyParams& p, hipStream_t stream);
 

@@ -23,6 +23,7 @@ constexpr int kMaxSplitTokens = 4096;   // the kernel keeps a split's page ids i
 
 struct Plan {
   bool mfma;         // MFMA kernels (bf16, head_dim 128) or the plain kernel
+  bool decode;       // the one-node (T = 1) kernel: whole contexts, no workspace
   bool stream;       // persistent MFMA kernel may run (workspace has its counters)
   int chunk;         // tokens per split
   int splits;        // max splits per (sequence, head)
@@ -48,8 +49,15 @@ inline bool use_stream_kernel(const tree_attn_desc& d, long long items, int n_cu
 inline Plan make_plan(const tree_attn_desc& d) {
   Plan p{};
   p.mfma = d.dtype == TA_BF16 && d.head_dim == 128 && !(d.flags & TA_FLAG_SIMPLE_KERNEL);
-  p.stream = p.mfma;
+  p.decode = p.mfma && d.t_max == 1 &&
+             !(d.flags & (TA_FLAG_GRID_KERNEL | TA_FLAG_PERSISTENT_KERNEL));
+  p.stream = p.mfma && !p.decode;
   const int max_ctx = d.max_ctx_len > 0 ? d.max_ctx_len : 1;
+  if (p.decode) {  // one workgroup streams a whole context; nothing to merge
+    p.chunk = max_ctx;
+    p.splits = 1;
+    return p;
+  }
   int chunk;
   if (d.split_tokens > 0) {
     chunk = d.split_tokens;

@@ -70,6 +70,10 @@ SPECS: Dict[str, WorkloadSpec] = {
     # large-batch stress with mixed tree sizes (1 = plain decode)
     "stress_b64": WorkloadSpec("stress_b64", 64, 32, 32, 128, "bf16",
                                (128, 8192), (1, 8, 26, 64), 4, 32000, 0.25),
+    # the plain-decode rows of the stress shape on their own: every sequence
+    # has only its root (T = 1)
+    "decode_b64": WorkloadSpec("decode_b64", 64, 32, 32, 128, "bf16",
+                               (128, 8192), (1,), 0, 32000, 0.25, t_max=1),
 }
 
 
