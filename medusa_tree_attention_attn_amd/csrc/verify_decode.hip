@@ -221,6 +221,11 @@ __global__ __launch_bounds__(kDecThreads) void verify_decode_kernel(VerifyParams
         const int j = j0 + u;
         if (j < my_pages && ids[u] >= 0) {
           const int tok0 = (p0 + wvu + kDecWaves * j) * kPage;
+          if (tok0 + kPage > ctx) {  // the context's last page: rows past its end
+#pragma unroll                         // are masked, and zeroed so a NaN there
+            for (int i = 0; i < 4; ++i)  // cannot reach 0 * V
+              if (tok0 + 4 * i + g >= ctx) ring[u].v[i] = u32x4{0u, 0u, 0u, 0u};
+          }
           float s[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {

@@ -18,9 +18,9 @@
 //     column, so the softmax row statistics are lane-local (plus one exchange
 //     between the two lane halves), and P^T feeds the PV product's B operand
 //     straight from the accumulators;
-//   * V is transposed in registers on its way into LDS, with the tokens of
-//     each 16-token block permuted so that a lane's PV A operand is one
-//     16-byte read;
+//   * V rows go to LDS as they are (rows past the context's end as zeros)
+//     and the PV A operand is read column-wise with the gfx950 transpose
+//     read (ds_read_b64_tr_b16);
 //   * online softmax in base 2 (q is pre-scaled by scale*log2 e); the running
 //     max only moves when a tile's max exceeds it by more than 8, which skips
 //     most rescales of the output accumulators;
@@ -95,13 +95,18 @@ __device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int til
   }
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& R, char* stage, int tid) {
+// Rows at or past n_rows (the tokens of the context's last page after its
+// end) are written as zeros: their scores are masked, but a NaN left in an
+// unused cache slot would still turn 0 * V into NaN in the P.V product.
+__device__ __forceinline__ void store_tile(const TileRegs& R, char* stage, int n_rows, int tid) {
   char* kb = stage + (tid >> 4) * kKRow + (tid & 15) * 16;
   char* vb = stage + kKBytes + (tid >> 4) * kVRow + (tid & 15) * 16;
+  const u32x4 z{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    *reinterpret_cast<u32x4*>(kb + 16 * p * kKRow) = R.k[p];
-    *reinterpret_cast<u32x4*>(vb + 16 * p * kVRow) = R.v[p];
+    const bool ok = 16 * p + (tid >> 4) < n_rows;
+    *reinterpret_cast<u32x4*>(kb + 16 * p * kKRow) = ok ? R.k[p] : z;
+    *reinterpret_cast<u32x4*>(vb + 16 * p * kVRow) = ok ? R.v[p] : z;
   }
 }
 
@@ -365,7 +370,8 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   // Tree tile -> stage 1 and context tile 0 -> stage 0 behind one barrier;
   // the next context tile's loads then overlap the tree tile's compute.
   if (sp == 0) store_tree_tile(stage1, TR, t_real, tid);
-  if (n_tiles > 0) store_tile(R[0], stage0, tid);
+  auto rows_of = [&](int t) { return min(kTile, c1 - (c0 + kTile * t)); };
+  if (n_tiles > 0) store_tile(R[0], stage0, rows_of(0), tid);
   __syncthreads();
   if (kDepth < n_tiles) load_ctx_tile(R[0], G, c0 + kTile * kDepth, c1, tid);
 #ifdef TA_TRACE
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
           char* cur = (t & 1) ? stage1 : stage0;
           char* nxt = (t & 1) ? stage0 : stage1;
           if (active) compute_tile<kFull>(st, qf, cur, L, kTile, 0ull);
-          store_tile(R[nu], nxt, tid);
+          store_tile(R[nu], nxt, rows_of(t + 1), tid);
           __syncthreads();
           if (t + 1 + kDepth < n_tiles)
             load_ctx_tile(R[nu], G, c0 + kTile * (t + 1 + kDepth), c1, tid);

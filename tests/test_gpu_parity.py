@@ -441,3 +441,40 @@ def test_two_chained_steps_match_oracle():
     real = wl.tree_parent != oracle.PAD_PARENT
     assert np.abs(out1.float().cpu().numpy() - r1)[real].max() <= ATOL
     assert np.abs(out2.float().cpu().numpy() - r2)[real].max() <= ATOL
+
+
+def _poison_unused_slots(wl):
+    """NaN in every cache slot the context does not cover: the tail of each
+    sequence's last page and all its pages past the context (the ones
+    reserved for the commit)."""
+    pool = wl.kv_pages.clone()
+    nan = float("nan")
+    for b in range(wl.spec.batch):
+        ctx = int(wl.ctx_lens[b])
+        for lb in range(wl.max_blocks):
+            blk = int(wl.block_table[b, lb])
+            if blk < 0:
+                continue
+            first = max(0, ctx - 16 * lb)       # slots of this page past the context
+            if first < 16:
+                pool[blk, :, :, first:] = nan
+    import dataclasses
+    return dataclasses.replace(wl, kv_pages=pool)
+
+
+@pytest.mark.parametrize("name,kw,kernel", [
+    ("vicuna7b_b16", dict(batch=4, heads=3, ctx_range=(1, 700)), "default"),
+    ("vicuna7b_b16", dict(batch=4, heads=3, ctx_range=(1, 700)), "persistent"),
+    ("vicuna7b_b16", dict(batch=4, heads=3, ctx_range=(1, 700)), "simple"),
+    ("stress_b64", dict(batch=6, heads=2, ctx_range=(1, 300)), "default"),
+    ("decode_b64", dict(batch=5, heads=2, ctx_range=(1, 500)), "default"),
+])
+def test_verify_ignores_nan_in_unused_cache_slots(name, kw, kernel):
+    """Slots past ctx_len are never part of the softmax; whatever they hold
+    (here NaN) must not reach the output."""
+    wl = _poison_unused_slots(make_workload(name, 15, **kw))
+    print(f"verify with NaN past the context: {name} {kw} kernel={kernel}", flush=True)
+    got = _verify_gpu(wl, KERNEL_FLAGS[kernel])
+    assert not np.isnan(got).any()
+    ref = oracle_verify_rows(wl, range(wl.spec.batch))
+    _check_rows(got, ref, wl, list(range(wl.spec.batch)))
