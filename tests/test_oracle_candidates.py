@@ -23,6 +23,22 @@ def test_topk_brute_force_with_ties():
         assert got[idx].tolist() == ref
 
 
+def test_topk_brute_force_with_nan_and_infinities():
+    """NaN ranks as -inf (after every number, among the -inf entries by
+    token); +inf ranks first."""
+    import math
+    rng = np.random.default_rng(2)
+    x = rng.integers(-2, 3, size=(20, 3, 19)).astype(np.float32)
+    x[rng.random(x.shape) < 0.2] = np.nan
+    x[rng.random(x.shape) < 0.1] = -np.inf
+    x[rng.random(x.shape) < 0.05] = np.inf
+    got = topk_tokens(x, 12)
+    for idx in np.ndindex(x.shape[:-1]):
+        row = [(-math.inf if math.isnan(v) else float(v)) for v in x[idx]]
+        ref = sorted(range(len(row)), key=lambda i: (-row[i], i))[:12]
+        assert got[idx].tolist() == ref
+
+
 def test_topk_matches_stable_sort():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((8, 5, 2000)).astype(np.float32)
