@@ -13,13 +13,17 @@ namespace ta {
 // are cut into splits of `chunk` tokens (a multiple of the 64-token tile)
 // whose partials a second kernel merges.  Each work item pays a prologue
 // (tree rows, q and tree k/v rows, RoPE rows, first tile) before it streams,
-// and each split costs a partial write and read, so the plan splits only as
-// far as needed to give every CU two resident work items (kTargetItems), and
-// never below kMinChunk tokens.
+// and each split costs a partial write and read plus a merge launch, so the
+// plan splits a context only while the work items still fit the CUs'
+// resident slots (two per CU, kTargetItems): (sequence, head) pairs times
+// splits <= kTargetItems, never below kMinChunk tokens.  Overshooting the
+// slots makes a second round of workgroups, which costs more than the balance
+// it buys (13B-shaped, 320 pairs of 4096 tokens: 136 us unsplit against
+// 170 us with two splits).
 constexpr int kTargetItems = 512;
 constexpr int kMinChunk = 256;
 constexpr int kTileTokens = 64;
-constexpr int kMaxSplitTokens = 4096;   // the kernel keeps a split's page ids in LDS
+constexpr int kMaxSplitTokens = 8192;   // the kernels keep a split's page ids in LDS
 
 struct Plan {
   bool mfma;         // MFMA kernels (bf16, head_dim 128) or the plain kernel
@@ -63,7 +67,7 @@ inline Plan make_plan(const tree_attn_desc& d) {
     chunk = d.split_tokens;
   } else {
     const long long bh = (long long)d.batch * d.num_heads;
-    const long long want = (kTargetItems + bh - 1) / bh;
+    const long long want = kTargetItems / bh;  // splits per pair that fit the slots
     const int splits = (int)(want < 1 ? 1 : (want > max_ctx ? max_ctx : want));
     chunk = (max_ctx + splits - 1) / splits;
     if (chunk < kMinChunk) chunk = kMinChunk;

@@ -302,14 +302,18 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   if (sp == 0) load_tree_raw(TR, p, b, hk, T, tid);
   const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks;
   const int max_pages = min(p.chunk / kPage, p.max_blocks - (c0 >> 4));
-  const int blk_raw = tid < max_pages ? table_row[(c0 >> 4) + tid] : -1;
+  static_assert(kMaxSplitPages <= 2 * kThreads, "two page ids per thread");
+  const int blk_raw0 = tid < max_pages ? table_row[(c0 >> 4) + tid] : -1;
+  const int blk_raw1 = tid + kThreads < max_pages ? table_row[(c0 >> 4) + tid + kThreads] : -1;
 
   const int ctx = clampi(ctx_raw, 0, p.max_ctx);
   const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
   if (sp >= nsplit) return;  // uniform: the whole workgroup leaves
   const int c1 = min(ctx, c0 + p.chunk);
   const int npages = (c1 - c0 + kPage - 1) / kPage;
-  if (tid < npages) s_pages[tid] = (blk_raw >= 0 && blk_raw < p.num_blocks) ? blk_raw : -1;
+  if (tid < npages) s_pages[tid] = (blk_raw0 >= 0 && blk_raw0 < p.num_blocks) ? blk_raw0 : -1;
+  if (tid + kThreads < npages)
+    s_pages[tid + kThreads] = (blk_raw1 >= 0 && blk_raw1 < p.num_blocks) ? blk_raw1 : -1;
 
   // Tree structure, one lane per node (every wavefront computes it).
   const bool real = lane < T && par != kPadParent;
