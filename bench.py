@@ -418,7 +418,7 @@ def main():
         write_traffic_record(*args.traffic_record, args.workload, args.seed)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the tree-verify step shards by sequence or head with no exchange; "
               "multi-GPU runs are not part of it)", file=sys.stderr)
         sys.exit(2)

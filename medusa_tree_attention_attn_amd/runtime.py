@@ -1,4 +1,4 @@
-"""Host-side driver of one Medusa tree-verify step on one GPU.
+"""Host-side runner of one Medusa tree-verify step on one GPU.
 
 `TreeVerifier` owns what a step needs besides the caller's tensors: the
 descriptor, the RoPE (cos, sin) table (filled by the library's own kernel)
