@@ -17,11 +17,14 @@
 // index where -inf matters.  Per segment:
 //   1. each thread finds its best element: the max value, then the smallest
 //      token holding it;
-//   2. tau = the k-th best of the 256 thread bests.  The k threads whose best
-//      is at least tau hold k elements >= tau, so the segment's k best
-//      elements are all >= tau; no other thread holds anything >= tau;
-//   3. the elements >= tau (at most k * values per thread) and the k winners
-//      of the previous segment go to an LDS list;
+//   2. each wavefront takes the k-th best of its 64 lanes' bests, and tau is
+//      the largest of these.  The wavefront that gives tau has k lanes whose
+//      bests are >= tau, so the segment's k best elements are all >= tau,
+//      and in every wavefront only lanes among its k best can hold anything
+//      >= tau;
+//   3. the elements >= tau (at most k lanes per wavefront times the values
+//      per lane) and the k winners of the previous segment go to an LDS
+//      list;
 //   4. the list's k best are ranked by counting, for each entry, the entries
 //      above it (rounds of workgroup max when the list is long).
 // Typical rows put a few dozen elements on the list; the bound holds for any
@@ -32,8 +35,9 @@
 namespace ta {
 namespace {
 
-constexpr int kCandThreads = 256;
-constexpr int kSegChunks = 16;  // 16-byte chunks per thread per segment
+constexpr int kCandThreads = 1024;  // 16 wavefronts: four per SIMD
+constexpr int kCandWaves = kCandThreads / 64;
+constexpr int kSegChunks = 4;  // 16-byte chunks per thread per segment
 
 __device__ __forceinline__ uint64_t elem_key(float v, int i) {
   uint32_t u = __float_as_uint(v != v ? -INFINITY : v);
@@ -88,12 +92,12 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
     int32_t* __restrict__ parent, int32_t* __restrict__ depth, int T) {
   constexpr int kPer = 16 / sizeof(S);
   constexpr int kSegValues = kSegChunks * kPer;           // per thread
-  constexpr int kCap = kMaxTopK * kSegValues + kMaxTopK;  // list bound
+  constexpr int kCap = kMaxTopK * kCandWaves * kSegValues + kMaxTopK;  // list bound
   __shared__ __align__(16) uint64_t s_list[kCap];
   __shared__ __align__(16) uint64_t s_best[kCandThreads];
-  __shared__ uint64_t s_red[kCandThreads / 64];
+  __shared__ uint64_t s_red[kCandWaves];
+  __shared__ uint64_t s_tauw[kCandWaves];
   __shared__ uint64_t s_win[kMaxTopK];
-  __shared__ uint64_t s_tau;
   __shared__ int s_n;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -127,24 +131,27 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
       best = first < V ? elem_key(-INFINITY, first) : 0ull;
     }
     s_best[tid] = best;
-    if (tid == 0) {
-      s_tau = 0ull;
-      s_n = 0;
-    }
+    if (lane == 0) s_tauw[wv] = 0ull;
+    if (tid == 0) s_n = 0;
     __syncthreads();
-    // 2. tau: the thread best with exactly k - 1 above it (0 when fewer than
-    //    k threads have elements: then every element is listed)
+    // 2. tau_w: the best of this wavefront's lanes with exactly k - 1 above
+    //    it (0 when fewer than k lanes have elements); tau = max over
+    //    wavefronts.  The wavefront holding that max has k lanes whose bests
+    //    are >= tau, so the segment's k best are all >= tau; in any
+    //    wavefront, only lanes among its k best reach tau.
     int rank = 0;
-    const ulonglong2* sb = reinterpret_cast<const ulonglong2*>(s_best);
+    const ulonglong2* sb = reinterpret_cast<const ulonglong2*>(s_best + 64 * wv);
 #pragma unroll 8
-    for (int q = 0; q < kCandThreads / 2; ++q) {
+    for (int q = 0; q < 32; ++q) {
       const ulonglong2 e = sb[q];
       rank += (e.x > best ? 1 : 0) + (e.y > best ? 1 : 0);
     }
-    if (rank == topk - 1 && best != 0ull) s_tau = best;
+    if (rank == topk - 1 && best != 0ull) s_tauw[wv] = best;
     __syncthreads();
+    uint64_t tau = 0ull;
+#pragma unroll
+    for (int w = 0; w < kCandWaves; ++w) tau = s_tauw[w] > tau ? s_tauw[w] : tau;
     // 3. the list: elements >= tau, then the previous segment's winners
-    const uint64_t tau = s_tau;
     if (best >= tau) {  // this thread holds elements >= tau
       const float tv = __uint_as_float((uint32_t)(tau >> 32) & 0x80000000u
                                            ? (uint32_t)(tau >> 32) & 0x7FFFFFFFu
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
         __syncthreads();
         w = s_red[0];
 #pragma unroll
-        for (int q = 1; q < kCandThreads / 64; ++q) w = s_red[q] > w ? s_red[q] : w;
+        for (int q = 1; q < kCandWaves; ++q) w = s_red[q] > w ? s_red[q] : w;
         if (tid == 0) s_win[r] = w;
         prev = w;
         __syncthreads();

@@ -83,9 +83,10 @@ def test_prepared_table_reused_across_calls():
 
 
 def test_candidates_adversarial_rows():
-    """Rows whose best values all sit in a few threads' share of the row (a
-    long candidate list: the rounds path), all-equal rows (ties decided by
-    token), rows of -inf and NaN, and a +inf."""
+    """Rows whose best values all sit in a few threads' share of the row,
+    rows that put thousands of elements on the candidate list (the rounds
+    path), all-equal rows (ties decided by token), rows of -inf and NaN, and
+    a +inf."""
     B, H, V, topk = 1, 4, 32000, 16
     choices = make_choices(9, n=60, max_depth=4, topk=topk)
     x = make_head_logits(B, H, V, seed=9, dtype=torch.float32)
@@ -99,7 +100,17 @@ def test_candidates_adversarial_rows():
     x[0, 2, 7] = float("inf")
     x[0, 3, ::3] = float("nan")
     logits = x.to(torch.bfloat16)
-    root = torch.tensor([4], dtype=torch.int32)
+    # Head 3 of a second sequence: lanes 0..15 of every wavefront hold values
+    # 100 + lane (16-byte chunk c = token // 8 goes to thread c % 1024, lane =
+    # thread % 64), so every wavefront's 16th-best lane is at 100 and about
+    # 15 x 32 elements per wavefront reach the bound: a list far longer than
+    # the workgroup (the rounds path).
+    y = make_head_logits(1, H, V, seed=19, dtype=torch.float32)
+    lane_of = (idx // 8) % 1024 % 64
+    y[0, 3] = torch.where(lane_of < 16, 100.0 + lane_of.float(), y[0, 3])
+    logits = torch.cat([logits, y.to(torch.bfloat16)], dim=0)
+    B = 2
+    root = torch.tensor([4, 9], dtype=torch.int32)
     wl = make_workload("vicuna7b_b16", 9, batch=B, heads=1, ctx_range=(16, 16))
     tv = verifier(wl)
     C, P, D = tv.candidates(choices, logits.cuda(), topk, root.cuda())
