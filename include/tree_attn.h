@@ -57,7 +57,8 @@
  *    (ctx_lens, block ids, tree structure, accepted paths) are bounds-checked
  *    inside the kernels: an out-of-range value never causes an out-of-bounds
  *    access, but the affected outputs are unspecified (ctx_len is clamped to
- *    [0, max_ctx_len]; an out-of-range page is skipped).
+ *    [0, max_ctx_len]; an out-of-range page id is never used as an address:
+ *    its tokens are skipped or read from page 0).
  *  - Calls are asynchronous; a launch failure is reported as TA_ERR_LAUNCH.
  *    Two calls that share a workspace must not run concurrently.
  */

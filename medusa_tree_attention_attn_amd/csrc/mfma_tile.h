@@ -39,6 +39,15 @@ constexpr int kVRow = 256 + 32;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kSlack = 8.0f;  // log2 units: p <= 2^8 before a rescale
 
+// Workgroup barrier that orders LDS only: LDS writes before it are visible to
+// every wavefront after it, while global loads already issued stay in flight
+// (a plain __syncthreads also waits for those).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 

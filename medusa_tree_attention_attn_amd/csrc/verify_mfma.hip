@@ -30,8 +30,9 @@
 //     pointer doubling across the lanes of a wavefront.
 // Splits of one (b, h) leave (m, l, O) partials in the workspace; a second,
 // small kernel merges them.  The prologue takes two dependent memory round
-// trips: everything that does not depend on ctx_len (tree rows, q row, tree
-// k/v rows, page ids), then the (cos, sin) rows and the first context tile.
+// trips: everything that does not depend on ctx_len (page ids, tree rows, q
+// row, tree k/v rows), then the (cos, sin) rows and the first two context
+// tiles; the tree tile is built and computed while those tiles load.
 #include "launch.h"
 #include "mfma_tile.h"
 #include "plan.h"
@@ -46,15 +47,11 @@ constexpr int kVBytes = kTile * kVRow;
 constexpr int kStageBytes = kKBytes + kVBytes;
 constexpr int kMaxSplitPages = kMaxSplitTokens / kPage;
 
-// Pipeline depth (context tiles in flight per workgroup) and the occupancy
-// the register budget is sized for (workgroups of 4 wavefronts per CU).
-#ifndef TA_PREFETCH_TILES
-#define TA_PREFETCH_TILES 1
-#endif
+// The occupancy the register budget is sized for (workgroups of 4
+// wavefronts per CU).
 #ifndef TA_WG_PER_CU
 #define TA_WG_PER_CU 2
 #endif
-constexpr int kDepth = TA_PREFETCH_TILES;
 
 // One tile's worth of global data held by a thread between load and store:
 // row tid/16 (of page p), 16-byte chunk tid%16, of the K and of the V plane.
@@ -64,34 +61,31 @@ struct TileRegs {
 };
 
 // Where the split's pages live: their physical ids were copied into LDS
-// (s_pages[i] = page of tokens c0 + 16 i, -1 when absent or out of range) so
-// the tile loop issues its KV loads without waiting on any table lookup.
+// (s_pages[i] = page of tokens c0 + 16 i; an id outside the pool reads page
+// 0) so the tile loop issues its KV loads without waiting on any table
+// lookup.
 struct Geo {
   const uint16_t* pages;
   const int* s_pages;
   int c0, hk, Hkv;
+  int last_page;  // index of the split's last page in s_pages
 };
 
-// Issue the loads of context tile [tile0, tile0 + 64); pages at or beyond c1
-// are never loaded (their rows hold zeros and are masked).  Page ids are
-// uniform, so page addresses are scalar; each lane adds a constant offset.
-__device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int tile0, int c1,
-                                              int tid) {
+// Issue the loads of context tile [tile0, tile0 + 64).  Pages past the
+// split's end load its last page again (L2 hits; store_tile zeroes their
+// rows), so the loads are unconditional and the compiler can count them.
+// Page ids are uniform, so page addresses are scalar; each lane adds a
+// constant offset.
+__device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int tile0, int tid) {
   const int pg0 = (tile0 - G.c0) >> 4;
   const int off = (tid >> 4) * kD + (tid & 15) * 8;
   const size_t v_plane = (size_t)G.Hkv * kPage * kD;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int blk =
-        tile0 + 16 * p < c1 ? __builtin_amdgcn_readfirstlane(G.s_pages[pg0 + p]) : -1;
-    if (blk >= 0) {
-      const uint16_t* kp = G.pages + page_row(blk, 0, G.hk, 0, G.Hkv, kD);
-      R.k[p] = *reinterpret_cast<const u32x4*>(kp + off);
-      R.v[p] = *reinterpret_cast<const u32x4*>(kp + v_plane + off);
-    } else {
-      R.k[p] = u32x4{0u, 0u, 0u, 0u};
-      R.v[p] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int blk = __builtin_amdgcn_readfirstlane(G.s_pages[min(pg0 + p, G.last_page)]);
+    const uint16_t* kp = G.pages + page_row(blk, 0, G.hk, 0, G.Hkv, kD);
+    R.k[p] = *reinterpret_cast<const u32x4*>(kp + off);
+    R.v[p] = *reinterpret_cast<const u32x4*>(kp + v_plane + off);
   }
 }
 
@@ -165,29 +159,25 @@ struct TreeRaw {
   u32x4 v[4];
   f32x4 cs[8];   // (cos, sin) of k = 16u .. 16u+15
 };
+// Rows past last_row read row last_row instead (store_tree_tile zeroes every
+// row at or past t_real): the loads are unconditional, so the wavefront
+// issues all of them without waiting on any.
 __device__ __forceinline__ void load_tree_raw(TreeRaw& TR, const VerifyParams& p, int b, int hk,
-                                              int t_real_hint, int tid) {
+                                              int last_row, int tid) {
   const int T = p.T;
   const uint16_t* kn = static_cast<const uint16_t*>(p.k_new);
   const uint16_t* vn = static_cast<const uint16_t*>(p.v_new);
-  const int j = tid >> 2, u = tid & 3;
-  if (j < t_real_hint) {
-    const uint16_t* row = kn + (((size_t)b * T + j) * p.Hkv + hk) * kD;
-    TR.k[0] = *reinterpret_cast<const u32x4*>(row + 16 * u);
-    TR.k[1] = *reinterpret_cast<const u32x4*>(row + 16 * u + 8);
-    TR.k[2] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u);
-    TR.k[3] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u + 8);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) TR.k[i] = u32x4{0u, 0u, 0u, 0u};
-  }
+  const int j = min(tid >> 2, last_row), u = tid & 3;
+  const uint16_t* row = kn + (((size_t)b * T + j) * p.Hkv + hk) * kD;
+  TR.k[0] = *reinterpret_cast<const u32x4*>(row + 16 * u);
+  TR.k[1] = *reinterpret_cast<const u32x4*>(row + 16 * u + 8);
+  TR.k[2] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u);
+  TR.k[3] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u + 8);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    const int jv = 16 * q4 + (tid >> 4);
-    TR.v[q4] = jv < t_real_hint
-                   ? *reinterpret_cast<const u32x4*>(
-                         vn + (((size_t)b * T + jv) * p.Hkv + hk) * kD + (tid & 15) * 8)
-                   : u32x4{0u, 0u, 0u, 0u};
+    const int jv = min(16 * q4 + (tid >> 4), last_row);
+    TR.v[q4] = *reinterpret_cast<const u32x4*>(vn + (((size_t)b * T + jv) * p.Hkv + hk) * kD +
+                                               (tid & 15) * 8);
   }
 }
 __device__ __forceinline__ void load_tree_rope(TreeRaw& TR, const float* rope, int pos_j, int tid) {
@@ -226,6 +216,39 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
     const int jv = 16 * q4 + (tid >> 4);
     *reinterpret_cast<u32x4*>(vb + 16 * q4 * kVRow) =
         jv < t_real ? TR.v[q4] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Output of an unsplit item.  The th = 0 wavefronts write their normalised
+// rows as bf16 (lane = query column, four consecutive dims per value group)
+// into a row-major tile in LDS; then all four wavefronts store whole
+// 256-byte rows of `out`, 16 bytes per lane, instead of 8-byte pieces of 32
+// rows per instruction.  Rows q >= T are not stored; padding rows are zeros.
+constexpr int kOutRow = 256 + 16;  // padded: the value-group writes spread over the banks
+__device__ __forceinline__ void stage_out(const WaveState& st, char* tile, int q, bool row_real,
+                                          int g) {
+  const float inv = (row_real && st.l > 0.f) ? 1.0f / st.l : 0.f;
+  char* row = tile + q * kOutRow;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 v4 = {st.o[dt][4 * rb] * inv, st.o[dt][4 * rb + 1] * inv,
+                        st.o[dt][4 * rb + 2] * inv, st.o[dt][4 * rb + 3] * inv};
+      *reinterpret_cast<u32x2*>(row + 2 * (32 * dt + 8 * rb + 4 * g)) =
+          __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4));
+    }
+}
+__device__ __forceinline__ void store_out(const char* tile, const VerifyParams& p, int b, int h,
+                                          int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;  // 16-byte chunk c % 16 of row c / 16
+    const int row = c >> 4, ch = c & 15;
+    if (row < p.T)
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) +
+                                (((size_t)b * p.T + row) * p.H + h) * kD + 8 * ch) =
+          *reinterpret_cast<const u32x4*>(tile + row * kOutRow + 16 * ch);
   }
 }
 
@@ -287,33 +310,43 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int q = 32 * qt + r32;
   const int c0 = sp * p.chunk;
 
-  // ---- round trip 1: ctx_len, tree rows, q row, tree k/v rows, page ids.
+  // ---- round trip 1: ctx_len, page ids, tree rows, then the q row and the
+  // tree k/v rows.  Every load is unconditional (row indices clamped into
+  // their arrays, values masked where they are used), so the wavefront issues
+  // them back to back; the LDS-only barrier below waits for the page ids and
+  // tree rows alone, and the q and tree k/v rows stay in flight into round
+  // trip 2.
   const int ctx_raw = p.ctx_lens[b];
-  const int par = lane < T ? p.tree_parent[(size_t)b * T + lane] : kPadParent;
-  const int dep = lane < T ? p.tree_depth[(size_t)b * T + lane] : 0;
-  QRaw Qr;
-  if (q < T) {
-    load_q_raw(Qr, static_cast<const uint16_t*>(p.q) + (((size_t)b * T + q) * p.H + h) * kD, g);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Qr.x[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  TreeRaw TR;
-  if (sp == 0) load_tree_raw(TR, p, b, hk, T, tid);
-  const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks;
+  // c0 < max(max_ctx, 1) <= 16 * max_blocks for every split of the plan, so
+  // max_pages >= 1 and the clamped page index stays inside the table row.
+  const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks + (c0 >> 4);
   const int max_pages = min(p.chunk / kPage, p.max_blocks - (c0 >> 4));
   static_assert(kMaxSplitPages <= 2 * kThreads, "two page ids per thread");
-  const int blk_raw0 = tid < max_pages ? table_row[(c0 >> 4) + tid] : -1;
-  const int blk_raw1 = tid + kThreads < max_pages ? table_row[(c0 >> 4) + tid + kThreads] : -1;
+  const int blk_raw0 = table_row[min(tid, max_pages - 1)];
+  const int blk_raw1 = table_row[min(tid + kThreads, max_pages - 1)];
+  const int row_l = min(lane, T - 1);
+  const int par_raw = p.tree_parent[(size_t)b * T + row_l];
+  const int dep_raw = p.tree_depth[(size_t)b * T + row_l];
+  QRaw Qr;  // rows q >= T are never used (row_real is false there)
+  load_q_raw(Qr,
+             static_cast<const uint16_t*>(p.q) + (((size_t)b * T + min(q, T - 1)) * p.H + h) * kD,
+             g);
+  TreeRaw TR;  // only split 0 uses it: the others read row 0 over and over
+  load_tree_raw(TR, p, b, hk, sp == 0 ? T - 1 : 0, tid);
 
   const int ctx = clampi(ctx_raw, 0, p.max_ctx);
   const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
   if (sp >= nsplit) return;  // uniform: the whole workgroup leaves
   const int c1 = min(ctx, c0 + p.chunk);
-  const int npages = (c1 - c0 + kPage - 1) / kPage;
-  if (tid < npages) s_pages[tid] = (blk_raw0 >= 0 && blk_raw0 < p.num_blocks) ? blk_raw0 : -1;
+  const int npages = (c1 - c0 + kPage - 1) / kPage;  // <= max_pages
+  // Entry 0 is written even for an empty split: the first two tiles load
+  // unconditionally.
+  if (tid < max(npages, 1))
+    s_pages[tid] = (tid < npages && blk_raw0 >= 0 && blk_raw0 < p.num_blocks) ? blk_raw0 : 0;
   if (tid + kThreads < npages)
-    s_pages[tid + kThreads] = (blk_raw1 >= 0 && blk_raw1 < p.num_blocks) ? blk_raw1 : -1;
+    s_pages[tid + kThreads] = (blk_raw1 >= 0 && blk_raw1 < p.num_blocks) ? blk_raw1 : 0;
+  const int par = lane < T ? par_raw : kPadParent;
+  const int dep = lane < T ? dep_raw : 0;
 
   // Tree structure, one lane per node (every wavefront computes it).
   const bool real = lane < T && par != kPadParent;
@@ -336,22 +369,21 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int pos_q = ctx + clampi(__shfl(dep, q), 0, T - 1);
   const int pos_j = ctx + clampi(__shfl(dep, tid >> 2), 0, T - 1);
 
-  __syncthreads();  // s_pages visible
+  lds_sync();  // s_pages visible; the q and tree k/v rows may still be in flight
 #ifdef TA_TRACE
   TA_STAMP(8);
 #endif
-  // ---- round trip 2: the first context tiles and the (cos, sin) rows.
-  Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv};
+  // ---- round trip 2: the (cos, sin) rows and context tile 0; tile 1 follows
+  // once q is rotated, and the tree tile is built and computed while it
+  // loads.
+  Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv, max(npages - 1, 0)};
   const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
-  // Tile j of the split travels through registers R[j % kDepth]: kDepth
-  // tiles are in flight from HBM while one is computed out of LDS.
-  TileRegs R[kDepth];
-#pragma unroll
-  for (int u = 0; u < kDepth; ++u)
-    if (u < n_tiles) load_ctx_tile(R[u], G, c0 + kTile * u, c1, tid);
   QRope Rq;
   load_q_rope(Rq, p.rope + (size_t)pos_q * kD, g);
-  if (sp == 0) load_tree_rope(TR, p.rope, pos_j, tid);
+  load_tree_rope(TR, p.rope, pos_j, tid);  // split 0 uses it; a valid row for every split
+  TileRegs R0;  // context tile 0
+  TileRegs R;   // context tile t + 1 while tile t is computed
+  load_ctx_tile(R0, G, c0, tid);  // unconditional: the compiler counts the loads
 
   u32x4 qf[8];
   if (row_real) {
@@ -360,6 +392,8 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) qf[s2] = u32x4{0u, 0u, 0u, 0u};
   }
+  // Issued once the q row and its table row are no longer held.
+  load_ctx_tile(R, G, c0 + kTile, tid);
 
   WaveState st;
   reset(st);
@@ -371,41 +405,33 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
 #ifdef TA_TRACE
   TA_STAMP(9);
 #endif
-  // Tree tile -> stage 1 and context tile 0 -> stage 0 behind one barrier;
-  // the next context tile's loads then overlap the tree tile's compute.
-  if (sp == 0) store_tree_tile(stage1, TR, t_real, tid);
-  auto rows_of = [&](int t) { return min(kTile, c1 - (c0 + kTile * t)); };
-  if (n_tiles > 0) store_tile(R[0], stage0, rows_of(0), tid);
-  __syncthreads();
-  if (kDepth < n_tiles) load_ctx_tile(R[0], G, c0 + kTile * kDepth, c1, tid);
-#ifdef TA_TRACE
-  TA_STAMP(10);
-#endif
+  // The tree tile goes through stage 1 while context tiles 0 and 1 load.
   if (sp == 0) {
+    store_tree_tile(stage1, TR, t_real, tid);
+    lds_sync();
+#ifdef TA_TRACE
+    TA_STAMP(10);
+#endif
     if (active) compute_tile<kTreeTile>(st, qf, stage1, L, kTile, anc_q);
-    __syncthreads();  // stage 1 is refilled by the loop's first store
   }
 #ifdef TA_TRACE
   TA_STAMP(11);
+#endif
+  auto rows_of = [&](int t) { return min(kTile, c1 - (c0 + kTile * t)); };
+  if (n_tiles > 0) store_tile(R0, stage0, rows_of(0), tid);
+  lds_sync();  // stage 0 filled, stage 1's tree reads done; tile 1 stays in flight
+#ifdef TA_TRACE
   TA_STAMP(4);
 #endif
   if (n_tiles > 0) {
     // Every tile but the last is full: one straight-line path, no masking.
-    for (int k0 = 0; k0 < n_tiles - 1; k0 += kDepth) {
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) {
-        const int t = k0 + u;
-        if (t < n_tiles - 1) {
-          const int nu = (u + 1) % kDepth;
-          char* cur = (t & 1) ? stage1 : stage0;
-          char* nxt = (t & 1) ? stage0 : stage1;
-          if (active) compute_tile<kFull>(st, qf, cur, L, kTile, 0ull);
-          store_tile(R[nu], nxt, rows_of(t + 1), tid);
-          __syncthreads();
-          if (t + 1 + kDepth < n_tiles)
-            load_ctx_tile(R[nu], G, c0 + kTile * (t + 1 + kDepth), c1, tid);
-        }
-      }
+    for (int t = 0; t < n_tiles - 1; ++t) {
+      char* cur = (t & 1) ? stage1 : stage0;
+      char* nxt = (t & 1) ? stage0 : stage1;
+      if (active) compute_tile<kFull>(st, qf, cur, L, kTile, 0ull);
+      store_tile(R, nxt, rows_of(t + 1), tid);
+      __syncthreads();
+      if (t + 2 < n_tiles) load_ctx_tile(R, G, c0 + kTile * (t + 2), tid);
     }
     // The last tile may end mid-tile.
     const int t = n_tiles - 1;
@@ -427,11 +453,18 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   float* mb = reinterpret_cast<float*>(smem) + qt * kParkFloats;  // [2][66][64]
   if (active && th == 1) park_state(st, mb, lane);
   __syncthreads();
-  if (th == 0) {
-    if (active) {
-      merge_state(st, mb, mb[64 * 64 + lane], mb[65 * 64 + lane], lane);
-      st.l += __shfl_xor(st.l, 32);
-    }
+  if (th == 0 && active) {
+    merge_state(st, mb, mb[64 * 64 + lane], mb[65 * 64 + lane], lane);
+    st.l += __shfl_xor(st.l, 32);
+  }
+  if (nsplit == 1) {  // uniform
+    static_assert(2 * kParkFloats * sizeof(float) + kTile * kOutRow <= 2 * kStageBytes,
+                  "output tile after the park area");
+    char* tile = smem + 2 * kParkFloats * sizeof(float);
+    if (th == 0) stage_out(st, tile, q, row_real, g);
+    __syncthreads();
+    store_out(tile, p, b, h, tid);
+  } else if (th == 0) {
     write_result(st, p, b, h, bh, sp, nsplit, q, T, row_real, g);
   }
 #ifdef TA_TRACE
