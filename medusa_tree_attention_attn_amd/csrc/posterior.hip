@@ -2,9 +2,10 @@
 // #1231: evaluate_posterior at LM-head temperature 0).
 //
 // One workgroup per (sequence, node) row streams the row's logits once with
-// 16-byte loads, all in flight before any compare, and reduces (value, token)
-// pairs: the larger value wins, the smaller token among equal values; NaN
-// never wins, and a row with nothing comparable gives token 0.
+// 16-byte loads (stream_row: the next chunk of every thread in flight while
+// one is compared) and reduces (value, token) pairs: the larger value wins,
+// the smaller token among equal values; NaN never wins, and a row with
+// nothing comparable gives token 0.
 //
 // The acceptance that consumes the tokens runs as a second launch: making
 // every row's token visible to one workgroup per sequence inside this launch
@@ -18,7 +19,7 @@
 namespace ta {
 namespace {
 
-constexpr int kArgThreads = 256;
+constexpr int kArgThreads = 256;  // threads per logits row
 
 struct Best {
   float v;
@@ -37,6 +38,65 @@ __device__ __forceinline__ void take(Best& b, float v, int i) {
   }
 }
 
+// Streams a row of nchunks 16-byte chunks through registers: thread tid
+// takes chunks i * kArgThreads + tid for i = 0, 1, ..., in increasing order,
+// in batches of Op::kBatch, with the next batch in flight while one is
+// consumed.  The loads are unconditional (an index past the row reads its
+// last chunk, which the consumer ignores), so the compiler's wait counts
+// cover them and a chunk is consumed as soon as its own load has arrived.
+// Op::batch(x, i0) consumes chunks i0 .. i0 + kBatch - 1 of the thread.
+// (Measured on 16 x 64 rows of 32000 bf16: one or two chunks per batch beat
+// four or eight, and 256 threads per row beat 512 or 1024.)
+template <typename Op>
+__device__ __forceinline__ void stream_row(const u32x4* __restrict__ src, int nchunks, int tid,
+                                           Op& op) {
+  constexpr int kB = Op::kBatch;
+  const int n = (nchunks + kArgThreads - 1) / kArgThreads;  // chunks per thread
+  const int last = nchunks - 1;
+  u32x4 ra[kB], rb[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u) ra[u] = src[min(u * kArgThreads + tid, last)];
+  // Keep batch a's loads ahead of batch b's: the wait for a then leaves b in
+  // flight, on the first pass as on every later one.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < kB; ++u) rb[u] = src[min((kB + u) * kArgThreads + tid, last)];
+  for (int i0 = 0; i0 < n; i0 += 2 * kB) {
+    op.batch(ra, i0);
+#pragma unroll
+    for (int u = 0; u < kB; ++u) ra[u] = src[min((i0 + 2 * kB + u) * kArgThreads + tid, last)];
+    op.batch(rb, i0 + kB);
+#pragma unroll
+    for (int u = 0; u < kB; ++u) rb[u] = src[min((i0 + 3 * kB + u) * kArgThreads + tid, last)];
+  }
+}
+
+// Argmax consumer of stream_row.
+template <typename S>
+struct ArgmaxOp {
+  static constexpr int kBatch = 1;
+  Best b;
+  int nchunks, tid;
+  __device__ __forceinline__ void batch(const u32x4 (&x)[kBatch], int i0) {
+    constexpr int kPer = 16 / sizeof(S);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = (i0 + u) * kArgThreads + tid;
+      if (c < nchunks) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (sizeof(S) == 2) {
+            take(b, bf16_lo(x[u][w]), c * kPer + 2 * w);
+            take(b, bf16_hi(x[u][w]), c * kPer + 2 * w + 1);
+          } else {
+            take(b, __uint_as_float(x[u][w]), c * kPer + w);
+          }
+        }
+      }
+    }
+  }
+};
+
 // Row argmax over V values; every thread of the workgroup returns the result.
 template <typename S>
 __device__ __forceinline__ int row_argmax(const S* row, int V, int tid, float* s_v, int* s_i) {
@@ -44,32 +104,9 @@ __device__ __forceinline__ int row_argmax(const S* row, int V, int tid, float* s
   constexpr int kPer = 16 / sizeof(S);  // values per 16-byte load
   const bool vec = (V % kPer) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   if (vec) {
-    const int nchunks = V / kPer;
-    const u32x4* src = reinterpret_cast<const u32x4*>(row);
-    constexpr int kUnroll = 16;
-    for (int c0 = 0; c0 < nchunks; c0 += kUnroll * kArgThreads) {
-      u32x4 x[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kArgThreads + tid;
-        x[u] = c < nchunks ? src[c] : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kArgThreads + tid;
-        if (c < nchunks) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            if (sizeof(S) == 2) {
-              take(b, bf16_lo(x[u][w]), c * kPer + 2 * w);
-              take(b, bf16_hi(x[u][w]), c * kPer + 2 * w + 1);
-            } else {
-              take(b, __uint_as_float(x[u][w]), c * kPer + w);
-            }
-          }
-        }
-      }
-    }
+    ArgmaxOp<S> op{b, V / kPer, tid};
+    stream_row(reinterpret_cast<const u32x4*>(row), V / kPer, tid, op);
+    b = op.b;
   } else {
     for (int i = tid; i < V; i += kArgThreads) take(b, ld(row, i), i);
   }
@@ -111,8 +148,8 @@ __global__ __launch_bounds__(kArgThreads) void vocab_argmax_kernel(const S* __re
 // Kernel 1, one workgroup per (sequence, node) row, one pass over the row in
 // base 2: with u = x * log2(e) / temperature, every thread keeps the running
 // max m of u, z = sum 2^(u - m) and s = sum 2^(u - m) (u - m).  Each batch
-// of up to 16 x 16 bytes per thread is held in registers, so its max is
-// taken first and the batch adds to (m, z, s) with one rescale
+// of two 16-byte chunks per thread (stream_row) is held in registers, so its
+// max is taken first and the batch adds to (m, z, s) with one rescale
 // (2^(m - m') when the max moves to m').  Since e^(y - M) = 2^(u - m) and
 // y - M = (u - m) ln 2 for y = x / temperature and its max M,
 //   lse = (m + log2 z) ln 2,   H = ln z - sum e^(y - M) (y - M) / z
@@ -155,6 +192,46 @@ __device__ __forceinline__ void add_term(Lse& t, float x, float c) {
   t.s = fmaf(e, d, t.s);
 }
 
+// Entropy consumer of stream_row: each batch of chunks is reduced
+// against its own max (c > 0, so the max of x is also the max of u = x c)
+// and merged into the running state with one rescale.
+template <typename S>
+struct EntropyOp {
+  static constexpr int kBatch = 2;
+  Lse a;
+  float c;
+  int nchunks, tid;
+  __device__ __forceinline__ void batch(const u32x4 (&x)[kBatch], int i0) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if ((i0 + u) * kArgThreads + tid < nchunks) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          mx = sizeof(S) == 2 ? fmaxf(mx, fmaxf(bf16_lo(x[u][w]), bf16_hi(x[u][w])))
+                              : fmaxf(mx, __uint_as_float(x[u][w]));
+      }
+    }
+    if (mx == -INFINITY) return;  // nothing but -inf (or no values): no mass
+    Lse t{mx * c, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if ((i0 + u) * kArgThreads + tid < nchunks) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (sizeof(S) == 2) {
+            add_term(t, bf16_lo(x[u][w]), c);
+            add_term(t, bf16_hi(x[u][w]), c);
+          } else {
+            add_term(t, __uint_as_float(x[u][w]), c);
+          }
+        }
+      }
+    }
+    merge_lse(a, t);
+  }
+};
+
 template <typename S>
 __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __restrict__ logits,
                                                                   int V, float c,
@@ -166,45 +243,9 @@ __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __res
   constexpr int kPer = 16 / sizeof(S);
   const bool vec = (V % kPer) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   if (vec) {
-    const int nchunks = V / kPer;
-    const u32x4* src = reinterpret_cast<const u32x4*>(row);
-    constexpr int kUnroll = 16;
-    for (int c0 = 0; c0 < nchunks; c0 += kUnroll * kArgThreads) {
-      u32x4 x[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int ch = c0 + u * kArgThreads + tid;
-        x[u] = ch < nchunks ? src[ch] : u32x4{0u, 0u, 0u, 0u};
-      }
-      // Batch max of the raw values (c > 0, so it is also the max of u).
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (c0 + u * kArgThreads + tid < nchunks) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            mx = sizeof(S) == 2 ? fmaxf(mx, fmaxf(bf16_lo(x[u][w]), bf16_hi(x[u][w])))
-                                : fmaxf(mx, __uint_as_float(x[u][w]));
-        }
-      }
-      if (mx == -INFINITY) continue;  // nothing but -inf (or no values): no mass
-      Lse t{mx * c, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (c0 + u * kArgThreads + tid < nchunks) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            if (sizeof(S) == 2) {
-              add_term(t, bf16_lo(x[u][w]), c);
-              add_term(t, bf16_hi(x[u][w]), c);
-            } else {
-              add_term(t, __uint_as_float(x[u][w]), c);
-            }
-          }
-        }
-      }
-      merge_lse(a, t);
-    }
+    EntropyOp<S> op{a, c, V / kPer, tid};
+    stream_row(reinterpret_cast<const u32x4*>(row), V / kPer, tid, op);
+    a = op.a;
   } else {
     for (int i = tid; i < V; i += kArgThreads) {
       const float x = ld(row, i);

@@ -34,6 +34,7 @@ def _argmax_gpu(wl, logits):
     ("stress_b64", 1, dict(batch=6), 1001, torch.bfloat16, 2),     # scalar path (odd vocab)
     ("stress_b64", 2, dict(batch=5), 12, torch.bfloat16, 4),       # tiny vocab, many ties
     ("vicuna7b_bs1", 3, {}, 250007, torch.bfloat16, 1),            # long rows, odd size
+    ("vicuna7b_b16", 4, dict(batch=2), 6144, torch.bfloat16, 2),   # 3 chunks per thread
 ])
 def test_vocab_argmax_bit_exact(name, seed, kw, vocab, dtype, ties):
     wl = make_workload(name, seed, heads=1, ctx_range=(16, 16), **kw)
@@ -53,9 +54,14 @@ def test_vocab_argmax_special_rows():
     logits[0, 3, 50] = float("inf")                   # ... the first one
     logits[0, 4] = 0.0
     logits[0, 4, 7] = -0.0                            # -0 == +0: token 0
+    logits[0, 5] = -float("inf")
+    logits[0, 5, :10] = float("nan")                  # first comparable value is -inf: 10
+    logits[0, 6] = -float("inf")
+    logits[0, 6, 1000:] = float("nan")
+    logits[0, 6, 3000] = -1e30                        # the only finite value: 3000
     got = _argmax_gpu(wl, logits)
     ref = vocab_argmax(logits)
-    assert got[0, :5].tolist() == [0, 0, ref[0, 2], 50, 0]
+    assert got[0, :7].tolist() == [0, 0, ref[0, 2], 50, 0, 10, 3000]
     assert np.array_equal(got, ref)
 
 
