@@ -190,10 +190,20 @@ __global__ __launch_bounds__(kDecThreads) void verify_decode_kernel(VerifyParams
   for (int p0 = 0; p0 < n_pages; p0 += kWinPages) {
     const int np = min(kWinPages, n_pages - p0);
     __syncthreads();  // the previous window's ids are no longer read
-    for (int i = tid; i < np; i += kDecThreads) {
-      const int pi = p0 + i;
-      const int blk = pi < p.max_blocks ? table[pi] : -1;
-      s_ids[i] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+    // All of the window's table loads are issued, unconditionally, before
+    // any is stored: one memory round trip, not one per pass, and no branch
+    // for the compiler's wait counts to merge over.  Indices are clamped into
+    // the window (n_pages <= max_blocks, since ctx <= max_ctx <= 16 *
+    // max_blocks); a clamped duplicate is an L2 hit and is not stored.
+    constexpr int kIdPasses = kWinPages / kDecThreads;
+    static_assert(kWinPages % kDecThreads == 0, "whole passes");
+    int raw[kIdPasses];
+#pragma unroll
+    for (int k = 0; k < kIdPasses; ++k) raw[k] = table[p0 + min(k * kDecThreads + tid, np - 1)];
+#pragma unroll
+    for (int k = 0; k < kIdPasses; ++k) {
+      const int i = k * kDecThreads + tid;
+      if (i < np) s_ids[i] = (raw[k] >= 0 && raw[k] < p.num_blocks) ? raw[k] : -1;
     }
     __syncthreads();
     const int my_pages = np > wvu ? (np - wvu + kDecWaves - 1) / kDecWaves : 0;
