@@ -8,7 +8,9 @@ tree_accept_greedy -> kv_commit_path instead) over one
 batch of the synthetic workload (default: batch 16, 32 heads, head_dim 128,
 bf16, contexts uniform in [256, 2048], trees of 64 nodes of depth <= 4,
 acceptance probability 0.3).  W untimed steps, then exactly K timed steps
-between two device synchronisations.  Inputs are resident in HBM before the
+launched from Python between two device synchronisations; the same K steps
+replayed as one captured HIP graph are reported beside them
+(ms_per_step_graph).  Inputs are resident in HBM before the
 timed region; the steps rotate over enough copies of the inputs and of the KV
 pool (>= 1 GB in total) that the 256 MB Infinity Cache cannot serve a repeat.
 
@@ -482,22 +484,48 @@ def main():
         torch.cuda.synchronize()
         log("calibration copies: 5 x 512 MiB device-to-device")
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
+    # The timed steps: W warmup steps, then K steps launched from Python
+    # between two events.  The same K steps are also captured as one HIP
+    # graph and replayed (what a serving loop that replays its launches
+    # would see); that figure is reported beside the eager one, and only if
+    # the replay leaves the same bits as the eager steps.
+    def time_steps(run):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps, time.perf_counter() - t
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    def eager_steps(first, n):
+        for k in range(first, first + n):
+            step(k)
+
+    eager_steps(0, args.warmup)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for k in range(args.steps):
-        step(args.warmup + k)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step, wall = time_steps(lambda: eager_steps(args.warmup, args.steps))
+    ms_per_step_graph = None
+    if args.steps > 0:
+        last = (args.warmup + args.steps - 1) % copies
+        st = sets[last]
+        bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+        ref = [t.clone() for t in (st["out"], L, P, st["pool"])]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            eager_steps(args.warmup, args.steps)
+        torch.cuda.synchronize()
+        g.replay()  # first replay: upload
+        torch.cuda.synchronize()
+        t_graph = time_steps(g.replay)[0]
+        if all(torch.equal(bits(x), bits(y))
+               for x, y in zip(ref, (st["out"], L, P, st["pool"]))):
+            ms_per_step_graph = t_graph
+        else:
+            log("graph replay differs from the eager steps: no graph figure")
+        del g, ref
 
     # Verify-kernel launch time for the roofline: the same launches back to
     # back on the library's stream (torch's current stream) between two
@@ -589,6 +617,7 @@ def main():
             "bytes_per_launch": nbytes["verify"],
             "avg_launch_us": round(v_avg * 1e3, 2),
         },
+        "ms_per_step_graph": (round(ms_per_step_graph, 5) if ms_per_step_graph else None),
         "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
         "per_call_us": {"verify": round(v_avg * 1e3, 2),
                         ("accept, commit" if args.separate_accept_commit else "accept_commit"):
