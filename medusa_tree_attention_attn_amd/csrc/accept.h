@@ -50,17 +50,34 @@ __device__ __forceinline__ Acceptance select_path(int par, bool edge_ok, bool in
 }
 
 // Greedy acceptance: edge parent(i) -> i passes iff cand_tokens[i] equals
-// the base model's greedy token after the parent.
+// the base model's greedy token after the parent.  Each lane loads its own
+// node's row entries (the index clamped into the tree, so the three loads
+// are unconditional and travel in one round trip) and takes the parent's
+// greedy token from the parent's lane.  Split in two so that a caller can
+// issue other loads between the row loads and their use.
+struct AcceptRows {
+  int par_raw, cand, greedy;
+};
+__device__ __forceinline__ AcceptRows load_accept_rows(const int32_t* __restrict__ node_argmax,
+                                                       const int32_t* __restrict__ cand_tokens,
+                                                       const int32_t* __restrict__ tree_parent,
+                                                       int b, int T, int i) {
+  const size_t ri = (size_t)b * T + min(i, T - 1);
+  return AcceptRows{tree_parent[ri], cand_tokens[ri], node_argmax[ri]};
+}
+__device__ __forceinline__ Acceptance accept_rows(const AcceptRows& r, int T, int i) {
+  const bool in_tree = i < T;
+  const int par = in_tree ? r.par_raw : kPadParent;
+  const bool linked = (i == 0) ? (par == -1) : (par >= 0 && par < i);
+  const int after_parent = __shfl(r.greedy, linked && i > 0 ? par : 0);  // parent < i < T
+  const bool match = linked && i > 0 && r.cand == after_parent;
+  return select_path(par, match, in_tree, i);
+}
 __device__ __forceinline__ Acceptance accept_wave(const int32_t* __restrict__ node_argmax,
                                                   const int32_t* __restrict__ cand_tokens,
                                                   const int32_t* __restrict__ tree_parent, int b,
                                                   int T, int i) {
-  const bool in_tree = i < T;
-  const size_t row = (size_t)b * T;
-  const int par = in_tree ? tree_parent[row + i] : kPadParent;
-  const bool linked = (i == 0) ? (par == -1) : (par >= 0 && par < i);
-  const bool match = linked && i > 0 && cand_tokens[row + i] == node_argmax[row + par];
-  return select_path(par, match, in_tree, i);
+  return accept_rows(load_accept_rows(node_argmax, cand_tokens, tree_parent, b, T, i), T, i);
 }
 
 __device__ __forceinline__ void write_acceptance(const Acceptance& a, int32_t* accept_len,

@@ -66,20 +66,35 @@ __device__ __forceinline__ void store8(float* p, const float (&y)[8]) {
   reinterpret_cast<f32x4*>(p)[1] = f32x4{y[4], y[5], y[6], y[7]};
 }
 
-// Path slot i of sequence b holds node n: write its K/V rows at ctx_len + i.
-template <typename S>
-__device__ __forceinline__ void commit_row(const CommitParams& p, int b, int i, int n) {
-  const int pos = clampi(p.ctx_lens[b], 0, p.max_ctx) + i;
+// Where path slot i of sequence b goes: position ctx_len + i and the page
+// holding it (block_table[b][pos / 16], row pos % 16).  Only ctx_len and the
+// table are read, so callers look the page up while the acceptance is still
+// being decided; the table index is clamped and the id is tested only where
+// the rows are stored (commit_row), so nothing here waits on the lookup.
+struct Dest {
+  int pos, blk;
+  bool in_table;  // pos has a table column and a RoPE row
+};
+__device__ __forceinline__ Dest commit_dest(const CommitParams& p, int b, int i, int ctx_raw) {
+  const int pos = clampi(ctx_raw, 0, p.max_ctx) + i;
   const int lb = pos / kPage;
-  if (lb >= p.max_blocks || pos >= p.rope_max_pos) return;
-  const int blk = p.block_table[(size_t)b * p.max_blocks + lb];
-  if (blk < 0 || blk >= p.num_blocks) return;
-  const int slot = pos % kPage;
+  const int blk = p.block_table[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)];
+  return Dest{pos, blk, lb < p.max_blocks && pos < p.rope_max_pos};
+}
+
+// Path slot at position d.pos holds node n: write its K/V rows there.  Every
+// row load (k_new, v_new, the (cos, sin) row) is issued before the page id
+// is tested, so the table lookup and the row loads share a round trip; the
+// stores are skipped when the page is out of range.
+template <typename S>
+__device__ __forceinline__ void commit_row(const CommitParams& p, int b, int n, const Dest& d) {
+  const bool ok = d.in_table && d.blk >= 0 && d.blk < p.num_blocks;
+  const int slot = d.pos % kPage;
   const int D = p.D, half = p.D / 2, groups = half / 8;
   const S* kn = static_cast<const S*>(p.k_new) + ((size_t)b * p.T + n) * p.Hkv * D;
   const S* vn = static_cast<const S*>(p.v_new) + ((size_t)b * p.T + n) * p.Hkv * D;
   S* pages = static_cast<S*>(p.kv_pages);
-  const float* cs = p.rope + (size_t)pos * D;
+  const float* cs = p.rope + (size_t)min(d.pos, p.rope_max_pos - 1) * D;
   for (int c = threadIdx.x; c < p.Hkv * groups; c += blockDim.x) {
     const int hk = c / groups, k0 = (c % groups) * 8;
     float x1[8], x2[8], cc[8], ss[8], y1[8], y2[8];
@@ -95,16 +110,18 @@ __device__ __forceinline__ void commit_row(const CommitParams& p, int b, int i, 
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) rope_pair_exact(x1[j], x2[j], cc[j], ss[j], y1[j], y2[j]);
-    S* krow = pages + page_row(blk, 0, hk, slot, p.Hkv, D);
-    store8(krow + k0, y1);
-    store8(krow + k0 + half, y2);
+    if (ok) {
+      S* krow = pages + page_row(d.blk, 0, hk, slot, p.Hkv, D);
+      store8(krow + k0, y1);
+      store8(krow + k0 + half, y2);
+    }
   }
   constexpr int kPer16 = 16 / sizeof(S);
   const int row_chunks = D / kPer16;
   for (int c = threadIdx.x; c < p.Hkv * row_chunks; c += blockDim.x) {
     const int hk = c / row_chunks, off = (c % row_chunks) * kPer16;
-    *reinterpret_cast<u32x4*>(pages + page_row(blk, 1, hk, slot, p.Hkv, D) + off) =
-        *reinterpret_cast<const u32x4*>(vn + (size_t)hk * D + off);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(vn + (size_t)hk * D + off);
+    if (ok) *reinterpret_cast<u32x4*>(pages + page_row(d.blk, 1, hk, slot, p.Hkv, D) + off) = v;
   }
 }
 
@@ -112,18 +129,19 @@ template <typename S>
 __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
   const int i = blockIdx.x, b = blockIdx.y;
   const int len = p.accept_len[b];
-  if (i >= len || len > p.T) return;
   const int n = p.accept_path[(size_t)b * p.T + i];
-  if (n < 0 || n >= p.T) return;
-  commit_row<S>(p, b, i, n);
+  const Dest d = commit_dest(p, b, i, p.ctx_lens[b]);
+  if (i >= len || len > p.T || n < 0 || n >= p.T) return;
+  commit_row<S>(p, b, n, d);
 }
 
 // Acceptance and commit in one launch: one workgroup per (path slot i,
-// sequence b).  Its first wavefront evaluates the sequence's tree (every
-// workgroup of the sequence gets the same answer); the workgroup of slot 0
-// publishes accept_len/accept_path, and each workgroup whose slot is on the
-// accepted path writes that row.  Same results as accept_kernel followed by
-// commit_kernel.
+// sequence b).  Every wavefront evaluates the sequence's tree (each gets the
+// same answer; the tree rows are L2 hits after the first), so no LDS or
+// barrier is needed; the slot's page is looked up meanwhile.  The workgroup
+// of slot 0 publishes accept_len/accept_path, and each workgroup whose slot
+// is on the accepted path writes that row.  Same results as accept_kernel
+// followed by commit_kernel.
 template <typename S>
 __global__ __launch_bounds__(256) void accept_commit_kernel(CommitParams p,
                                                             const int32_t* __restrict__ node_argmax,
@@ -131,17 +149,18 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitParams p,
                                                             const int32_t* __restrict__ tree_parent,
                                                             int32_t* __restrict__ accept_len,
                                                             int32_t* __restrict__ accept_path) {
-  __shared__ int s_node;
-  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  if (tid < 64) {
-    const Acceptance a = accept_wave(node_argmax, cand_tokens, tree_parent, b, p.T, tid);
-    if (i == 0) write_acceptance(a, accept_len, accept_path, b, p.T, tid);
-    const uint64_t at_i = __ballot(a.in_tree && ((a.path >> tid) & 1ull) && a.depth == i);
-    if (tid == 0) s_node = at_i ? __builtin_ctzll(at_i) : -1;
-  }
-  __syncthreads();
-  const int n = s_node;
-  if (n >= 0) commit_row<S>(p, b, i, n);
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  // Round trip 1: the tree rows and ctx_len; then the slot's table entry,
+  // issued before the rows are used.
+  const AcceptRows rows = load_accept_rows(node_argmax, cand_tokens, tree_parent, b, p.T, lane);
+  const int ctx_raw = p.ctx_lens[b];
+  __builtin_amdgcn_sched_barrier(0);
+  const Dest d = commit_dest(p, b, i, ctx_raw);
+  __builtin_amdgcn_sched_barrier(0);
+  const Acceptance a = accept_rows(rows, p.T, lane);
+  if (i == 0 && tid < 64) write_acceptance(a, accept_len, accept_path, b, p.T, lane);
+  const uint64_t at_i = __ballot(a.in_tree && ((a.path >> lane) & 1ull) && a.depth == i);
+  if (at_i != 0ull) commit_row<S>(p, b, __builtin_ctzll(at_i), d);
 }
 
 // (cos, sin) of pos * base^(-2k/d): angle in fp64, one rounding to fp32.
