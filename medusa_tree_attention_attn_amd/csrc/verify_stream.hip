@@ -82,10 +82,15 @@ struct Fetch {
 };
 
 // LDS-only barrier: LDS writes done, then s_barrier.  Loads that fill the
-// other stage stay in flight (a plain __syncthreads would wait for them).
+// other stage stay in flight (a plain __syncthreads would wait for them, and
+// so would a workgroup fence on the local address space, which counts the
+// direct-to-LDS loads as LDS writes).  The signal fences keep the compiler
+// from moving any memory access across the barrier; they emit no code.
 __device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
   __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 // Everything this wavefront issued has landed (including its direct-to-LDS loads).
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0070); }
