@@ -480,10 +480,13 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
 }
 
 // Merge the (m, l, O) partials of every (sequence, head) whose context took
-// more than one split, and write its `out` rows (padding rows as zeros).  A
-// separate launch: the kernel boundary makes every split's partials visible,
-// where a device-wide fence inside the verify kernel would write back and
-// invalidate the L2 of its XCD once per workgroup.
+// more than one split, and write its `out` rows (padding rows as zeros).
+// One workgroup per 16 rows of a (sequence, head), so that a small batch
+// still spreads the partial reads over many CUs.  A separate launch: the
+// kernel boundary makes every split's partials visible, where a device-wide
+// fence inside the verify kernel would write back and invalidate the L2 of
+// its XCD once per workgroup.
+constexpr int kCombineRows = 16;  // rows of one (sequence, head) per combine workgroup
 __global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int bh = blockIdx.x;
@@ -495,32 +498,48 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
   const int par = lane < T ? p.tree_parent[(size_t)b * T + lane] : kPadParent;
   const uint64_t real_mask = __ballot(lane < T && par != kPadParent);
   const int t_real = real_mask == ~0ull ? 64 : __builtin_ctzll(~real_mask);
-  const int cq = tid >> 2, part = tid & 3;
+  // Thread: row cq of this workgroup's 16, dims 8 ch .. 8 ch + 7.
+  const int cq = kCombineRows * blockIdx.y + (tid >> 4), ch = tid & 15;
   if (cq >= T) return;
-  uint16_t* orow =
-      static_cast<uint16_t*>(p.out) + (((size_t)b * T + cq) * p.H + h) * kD + 32 * part;
-  f32x8 acc[4] = {f32x8{}, f32x8{}, f32x8{}, f32x8{}};
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + (((size_t)b * T + cq) * p.H + h) * kD + 8 * ch;
+  f32x8 acc = {};
   float L = 0.f;
   if (cq < t_real) {
+    // Splits are read in unrolled groups of four whose loads are all issued
+    // before any is used (one memory round trip per group, not per split);
+    // an index past the last split reads the last one again and is given no
+    // weight.
     const size_t row0 = (size_t)bh * p.splits * T + cq;
+    auto row_of = [&](int s) { return row0 + (size_t)min(s, nsplit - 1) * T; };
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[row0 + (size_t)s * T].x);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    for (int s = 0; s < nsplit; ++s) {
-      const size_t row = row0 + (size_t)s * T;
-      const float2 ml = p.ws_ml[row];
-      const float w = __builtin_amdgcn_exp2f(ml.x - Mu);
-      L += w * ml.y;
-      const f32x8* src = reinterpret_cast<const f32x8*>(p.ws_o + row * kD + 32 * part);
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      float m[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += w * src[c];
+      for (int u = 0; u < 4; ++u) m[u] = p.ws_ml[row_of(s0 + u)].x;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) M = fmaxf(M, m[u]);  // a repeated split leaves the max as is
+    }
+    const float Mu = M == -INFINITY ? 0.f : M;
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      float2 ml[4];
+      f32x8 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t row = row_of(s0 + u);
+        ml[u] = p.ws_ml[row];
+        o[u] = reinterpret_cast<const f32x8*>(p.ws_o + row * kD)[ch];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the group's loads all go out first
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = s0 + u < nsplit ? __builtin_amdgcn_exp2f(ml[u].x - Mu) : 0.f;
+        L += w * ml[u].y;
+        acc += w * o[u];
+      }
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    *reinterpret_cast<u32x4*>(orow + 8 * c) =
-        __builtin_bit_cast(u32x4, __builtin_convertvector(acc[c] * inv, bf16x8));
+  *reinterpret_cast<u32x4*>(orow) = __builtin_bit_cast(u32x4, __builtin_convertvector(acc * inv, bf16x8));
 }
 
 }  // namespace
@@ -539,7 +558,10 @@ hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_split_combine(const VerifyParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.B * p.H)), dim3(kThreads), 0, stream, p);
+  static_assert(kThreads == 16 * kCombineRows, "16 threads per row");
+  const unsigned row_groups = (unsigned)((p.T + kCombineRows - 1) / kCombineRows);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.B * p.H), row_groups), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
