@@ -289,18 +289,32 @@ def _oracle_timing(wl):
                 seconds=dt)
 
 
-def time_calls(fn, n_inputs, reps, outputs):
+def _prewarm(fn, ms):
+    """Untimed calls fn(k), k = 0, 1, ..., for `ms` of wall time; the host
+    waits every 8 calls so it cannot run far ahead of the GPU.  The GPU's
+    clocks ramp up over the first tens of milliseconds of sustained load
+    and drop again while it idles."""
+    t_end = time.perf_counter() + ms / 1e3
+    k = 0
+    while time.perf_counter() < t_end:
+        fn(k)
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_calls(fn, n_inputs, reps, outputs, prewarm_ms=100.0):
     """Average microseconds per call of fn(k) (k picks input k % n_inputs):
       eager  back-to-back calls from Python between two events: what a
              caller sees, host overhead included when it exceeds the GPU's
              share;
       gpu    the same calls captured once into a HIP graph and replayed:
              the kernels' own time (launch gaps of a replayed graph only).
-    The graph's outputs after the replay must equal the eager ones (both
-    end on the same input); otherwise gpu is None."""
-    for k in range(5):
-        fn(k % n_inputs)
-    torch.cuda.synchronize()
+    Each timing follows prewarm_ms of untimed calls of the same kind.  The
+    graph's outputs after the replay must equal the eager ones (both end on
+    the same input); otherwise gpu is None."""
+    _prewarm(lambda k: fn(k % n_inputs), prewarm_ms)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for k in range(reps):
@@ -314,6 +328,7 @@ def time_calls(fn, n_inputs, reps, outputs):
         for k in range(reps):
             fn(k % n_inputs)
     torch.cuda.synchronize()
+    _prewarm(lambda k: g.replay(), prewarm_ms)
     gpu = []
     for _ in range(3):
         for t in outputs:
@@ -517,14 +532,7 @@ def main():
     # fill prewarm_ms, so it sees the steady state a serving loop runs at;
     # the host waits every 8 calls so it cannot run far ahead of the GPU.
     def prewarm(fn):
-        t_end = time.perf_counter() + args.prewarm_ms / 1e3
-        k = 0
-        while time.perf_counter() < t_end:
-            fn(k)
-            k += 1
-            if k % 8 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
+        _prewarm(fn, args.prewarm_ms)
 
     prewarm(step)
     eager_steps(0, args.warmup)
