@@ -252,38 +252,50 @@ __device__ __forceinline__ void store_out(const char* tile, const VerifyParams& 
   }
 }
 
-// Launch slot -> (sequence, head, split).  With one split per pair and at
-// most 64 sequences, pairs are ranked by context length (longest first, one
-// sequence's heads together).  When there are between one and two pairs per
-// CU, slots 0..n_cu-1 take the longest pairs and slot n_cu + i takes the i-th
-// shortest: the dispatcher fills every CU with slots i and i + n_cu, so each
-// CU then holds one long and one short pair and about the average number of
-// tiles.  With more pairs than that, longest-first order lets the dispatcher
-// hand the short tail to whichever CU frees up first.  Otherwise (splits, or
-// more than 64 sequences) the order is (sequence, head) major, split minor.
-// Every lane of the wavefront takes part (lane = sequence).
+// Launch slot -> (sequence, head, split).  A (sequence, split) group holds H
+// work items of the same length (the split's tokens).  With at most 64
+// groups, the groups that exist are ranked by length (longest first, equal
+// lengths in (sequence, split) order) and each group's heads take
+// consecutive slots; slots past the real items leave at once.  When there are
+// between one and two items per CU, slots 0..n_cu-1 take the longest items
+// and slot n_cu + i takes the i-th shortest: the dispatcher fills every CU
+// with slots i and i + n_cu, so each CU then holds one long and one short item
+// and about the average number of tiles.  With more items than that,
+// longest-first order lets the dispatcher hand the short tail to whichever CU
+// frees up first.  With more than 64 groups the order is (sequence, head)
+// major, split minor.  Every lane of the wavefront takes part (lane = group).
 __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int lane, int& b,
                                             int& h, int& sp) {
-  const int N = p.B * p.H;
-  if (p.B > 64 || p.splits != 1 || p.n_cu <= 0) {
+  const int G = p.B * p.splits;
+  if (G > 64 || p.n_cu <= 0) {
     b = (slot / p.splits) / p.H;
     h = (slot / p.splits) % p.H;
     sp = slot % p.splits;
     return true;
   }
-  sp = 0;
+  int len = -1;  // tokens of the group's split; -1: the split does not exist
+  if (lane < G) {
+    const int j = lane / p.splits, s = lane - j * p.splits;
+    const int c = clampi(p.ctx_lens[j], 0, p.max_ctx);
+    const int n = c == 0 ? 1 : (c + p.chunk - 1) / p.chunk;
+    if (s < n) len = min(p.chunk, c - s * p.chunk);
+  }
+  const int N = __popcll(__ballot(len >= 0)) * p.H;
+  if (slot >= N) return false;  // uniform
   int r = slot;
   if (N > p.n_cu && N <= 2 * p.n_cu && slot >= p.n_cu) r = N - 1 - (slot - p.n_cu);
-  const int ctx_l = lane < p.B ? p.ctx_lens[lane] : -1;
   int rank = 0;
-  for (int j = 0; j < p.B; ++j) {
-    const int cj = __shfl(ctx_l, j);
-    rank += (cj > ctx_l) || (cj == ctx_l && j < lane);
+  for (int j = 0; j < G; ++j) {
+    const int lj = __shfl(len, j);
+    rank += (lj > len) || (lj == len && j < lane);
   }
-  const int j = r / p.H;
-  h = r % p.H;
-  b = __builtin_ctzll(__ballot(lane < p.B && rank == j));
-  return r < N;
+  const int gr = r / p.H;
+  h = r - gr * p.H;
+  const uint64_t hit = __ballot(lane < G && rank == gr);
+  const int grp = hit ? __builtin_ctzll(hit) : 0;
+  b = grp / p.splits;
+  sp = grp - b * p.splits;
+  return true;
 }
 
 #ifdef TA_TRACE

@@ -106,6 +106,18 @@ def test_verify_split_sizes(split_tokens, kernel):
     _check_rows(got, ref, wl, list(range(4)))
 
 
+def test_verify_split_ranked_long_short_pairs():
+    """Split items ranked by length and paired long with short: 8 sequences x
+    24 heads with 512-token splits give 17 (sequence, split) groups, 408 work
+    items, between one and two per CU on a 256-CU device, so the launch slots
+    past the CU count take the shortest items in reverse order."""
+    wl = make_workload("vicuna7b_b16", 21, batch=8, heads=24, ctx_range=(0, 1500))
+    print("verify ranked split items, 8x24, split_tokens=512, grid kernel", flush=True)
+    got = _verify_gpu(wl, flags=KERNEL_FLAGS["grid"], split_tokens=512)
+    ref = oracle_verify_rows(wl, range(8))
+    _check_rows(got, ref, wl, list(range(8)))
+
+
 def test_verify_repeated_calls_reuse_workspace():
     """The arrival counters reset themselves: repeated calls on one workspace
     give identical results."""
