@@ -44,6 +44,7 @@ __device__ __forceinline__ void take(Best& b, float v, int i) {
 // consumed.  The loads are unconditional (an index past the row reads its
 // last chunk, which the consumer ignores), so the compiler's wait counts
 // cover them and a chunk is consumed as soon as its own load has arrived.
+// The rows are read once: the loads carry the non-temporal hint.
 // Op::batch(x, i0) consumes chunks i0 .. i0 + kBatch - 1 of the thread.
 // (Measured on 16 x 64 rows of 32000 bf16: one or two chunks per batch beat
 // four or eight, and 256 threads per row beat 512 or 1024.)
@@ -55,19 +56,22 @@ __device__ __forceinline__ void stream_row(const u32x4* __restrict__ src, int nc
   const int last = nchunks - 1;
   u32x4 ra[kB], rb[kB];
 #pragma unroll
-  for (int u = 0; u < kB; ++u) ra[u] = src[min(u * kArgThreads + tid, last)];
+  for (int u = 0; u < kB; ++u) ra[u] = __builtin_nontemporal_load(&src[min(u * kArgThreads + tid, last)]);
   // Keep batch a's loads ahead of batch b's: the wait for a then leaves b in
   // flight, on the first pass as on every later one.
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < kB; ++u) rb[u] = src[min((kB + u) * kArgThreads + tid, last)];
+  for (int u = 0; u < kB; ++u)
+    rb[u] = __builtin_nontemporal_load(&src[min((kB + u) * kArgThreads + tid, last)]);
   for (int i0 = 0; i0 < n; i0 += 2 * kB) {
     op.batch(ra, i0);
 #pragma unroll
-    for (int u = 0; u < kB; ++u) ra[u] = src[min((i0 + 2 * kB + u) * kArgThreads + tid, last)];
+    for (int u = 0; u < kB; ++u)
+      ra[u] = __builtin_nontemporal_load(&src[min((i0 + 2 * kB + u) * kArgThreads + tid, last)]);
     op.batch(rb, i0 + kB);
 #pragma unroll
-    for (int u = 0; u < kB; ++u) rb[u] = src[min((i0 + 3 * kB + u) * kArgThreads + tid, last)];
+    for (int u = 0; u < kB; ++u)
+      rb[u] = __builtin_nontemporal_load(&src[min((i0 + 3 * kB + u) * kArgThreads + tid, last)]);
   }
 }
 

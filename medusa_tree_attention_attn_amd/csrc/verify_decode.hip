@@ -73,12 +73,15 @@ struct State {
   float o[8];
 };
 
+// The pages are read once: the loads carry the non-temporal hint (batch 64,
+// contexts 128..8192: 639 against 698 us per launch).
 __device__ __forceinline__ void load_page(Page& P, const uint16_t* kbase, size_t v_plane,
                                           int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    P.k[i] = *reinterpret_cast<const u32x4*>(kbase + 512 * i + 8 * lane);
-    P.v[i] = *reinterpret_cast<const u32x4*>(kbase + v_plane + 512 * i + 8 * lane);
+    P.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + 512 * i + 8 * lane));
+    P.v[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(kbase + v_plane + 512 * i + 8 * lane));
   }
 }
 

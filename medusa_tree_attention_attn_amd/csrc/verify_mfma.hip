@@ -107,7 +107,10 @@ __device__ __forceinline__ void store_tile(const TileRegs& R, char* stage, int n
 }
 
 // Q^T fragments of query row q for k-steps 0..7 (chunk 2*ks + g), rotated at
-// pos and pre-scaled by scale*log2 e.  Chunk c and chunk c+8 hold the RoPE
+// pos and pre-scaled by scale*log2 e.  (The two wavefronts of a query tile
+// read the same rows, and rows past the tree's end reread its last row: these
+// loads keep the default cache policy, since the non-temporal hint made the
+// rereads miss and cost 2.6 us per launch on the 7B-shaped batch-16 shape.)  Chunk c and chunk c+8 hold the RoPE
 // partners d and d+64, so the rotation stays inside the lane.  Loaded in two
 // steps so that the row and its (cos, sin) table row travel in different
 // round trips of the prologue.

@@ -43,6 +43,7 @@ constexpr int kJStage = 2 * kJKBytes;               // K then V rows (64 KB)
 constexpr int kQBufU4 = 2 * 8 * 64;                 // q fragments of a unit (u32x4 units)
 constexpr int kPagesMax = kMaxSplitTokens / kPage;  // page ids of one split
 constexpr int kAhead = 3;                           // jobs left when the next unit is taken
+constexpr int kNt = 2;  // cache-policy operand of the direct-to-LDS loads: non-temporal (read once)
 constexpr int kParkO = 64 * 64;                     // O^T of one wavefront (floats)
 static_assert(2 * kJStage + 2 * kPagesMax * 4 + kQBufU4 * 16 + 4 * 2 * 64 * 4 + 16 <= 163840,
               "LDS budget");
@@ -191,7 +192,7 @@ __device__ __forceinline__ void load_q(const VerifyParams& p, const Unit& U, con
         const int c = ks < 4 ? 2 * ks + (lane >> 5) : 8 + 2 * (ks - 4) + (lane >> 5);
         __builtin_amdgcn_global_load_lds(
             row + 8 * c, (__attribute__((address_space(3))) void*)(qbuf + (qt * 8 + ks) * 64), 16,
-            0, 0);
+            0, kNt);
       }
     }
   }
@@ -248,9 +249,10 @@ __device__ __forceinline__ void issue_ctx_job(char* stage, const VerifyParams& p
       const int c = (lane & 15) ^ (4 * rq + i);
       const int off = (4 * i + rq) * kD + 8 * c;
       __builtin_amdgcn_global_load_lds(
-          kp + off, (__attribute__((address_space(3))) void*)(krows + i * 1024), 16, 0, 0);
+          kp + off, (__attribute__((address_space(3))) void*)(krows + i * 1024), 16, 0, kNt);
       __builtin_amdgcn_global_load_lds(
-          vp + off, (__attribute__((address_space(3))) void*)(krows + kJKBytes + i * 1024), 16, 0, 0);
+          vp + off, (__attribute__((address_space(3))) void*)(krows + kJKBytes + i * 1024), 16, 0,
+          kNt);
     }
   } else {
 #pragma unroll
@@ -297,10 +299,10 @@ __device__ __forceinline__ void issue_tree_job(char* stage, const VerifyParams& 
       const int c = (lane & 15) ^ swz(j);
       const size_t off = (((size_t)U.b * T + j) * p.Hkv + U.hk) * kD + 8 * c;
       __builtin_amdgcn_global_load_lds(
-          kn + off, (__attribute__((address_space(3))) void*)(stage + quad * 1024), 16, 0, 0);
+          kn + off, (__attribute__((address_space(3))) void*)(stage + quad * 1024), 16, 0, kNt);
       __builtin_amdgcn_global_load_lds(
           vn + off, (__attribute__((address_space(3))) void*)(stage + kJKBytes + quad * 1024), 16,
-          0, 0);
+          0, kNt);
     }
   }
 #pragma unroll
