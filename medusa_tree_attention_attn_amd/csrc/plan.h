@@ -16,12 +16,13 @@ namespace ta {
 // and each split costs a partial write and read plus a merge launch, so the
 // plan splits a context only while the work items still fit the CUs'
 // resident slots (two per CU, kTargetItems): (sequence, head) pairs times
-// splits <= kTargetItems, never below kMinChunk tokens.  Overshooting the
-// slots makes a second round of workgroups, which costs more than the balance
-// it buys (13B-shaped, 320 pairs of 4096 tokens: 136 us unsplit against
-// 170 us with two splits).
+// splits <= kTargetItems, never below kMinChunk tokens (batch 1, 32 heads,
+// 1024 tokens: 17.0 us with 128-token splits, 17.8 with 256, 19.7 with
+// 384).  Overshooting the slots makes a second round of workgroups, which
+// costs more than the balance it buys (13B-shaped, 320 pairs of 4096
+// tokens: 136 us unsplit against 170 us with two splits).
 constexpr int kTargetItems = 512;
-constexpr int kMinChunk = 256;
+constexpr int kMinChunk = 128;
 constexpr int kTileTokens = 64;
 constexpr int kMaxSplitTokens = 8192;   // the kernels keep a split's page ids in LDS
 

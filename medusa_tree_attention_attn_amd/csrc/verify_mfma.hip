@@ -509,10 +509,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.H, h = bh % p.H;
   const int T = p.T;
-  const int ctx = clampi(p.ctx_lens[b], 0, p.max_ctx);
+  // ctx_len and the tree rows in one round trip (the row index is clamped
+  // into the array and masked below).
+  const int ctx_raw = p.ctx_lens[b];
+  const int par_raw = p.tree_parent[(size_t)b * T + min(lane, T - 1)];
+  const int ctx = clampi(ctx_raw, 0, p.max_ctx);
   const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
   if (nsplit == 1) return;
-  const int par = lane < T ? p.tree_parent[(size_t)b * T + lane] : kPadParent;
+  const int par = lane < T ? par_raw : kPadParent;
   const uint64_t real_mask = __ballot(lane < T && par != kPadParent);
   const int t_real = real_mask == ~0ull ? 64 : __builtin_ctzll(~real_mask);
   // Thread: row cq of this workgroup's 16, dims 8 ch .. 8 ch + 7.
@@ -523,20 +527,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
   float L = 0.f;
   if (cq < t_real) {
     // Splits are read in unrolled groups of four whose loads are all issued
-    // before any is used (one memory round trip per group, not per split);
-    // an index past the last split reads the last one again and is given no
-    // weight.
+    // before any is used (one memory round trip per group, not per split),
+    // and merged online: the running max moves to the group's max and the
+    // sums so far are rescaled.  An index past the last split reads the last
+    // one again and is given no weight.
     const size_t row0 = (size_t)bh * p.splits * T + cq;
     auto row_of = [&](int s) { return row0 + (size_t)min(s, nsplit - 1) * T; };
     float M = -INFINITY;
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
-      float m[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) m[u] = p.ws_ml[row_of(s0 + u)].x;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) M = fmaxf(M, m[u]);  // a repeated split leaves the max as is
-    }
-    const float Mu = M == -INFINITY ? 0.f : M;
     for (int s0 = 0; s0 < nsplit; s0 += 4) {
       float2 ml[4];
       f32x8 o[4];
@@ -547,12 +544,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
         o[u] = reinterpret_cast<const f32x8*>(p.ws_o + row * kD)[ch];
       }
       __builtin_amdgcn_sched_barrier(0);  // the group's loads all go out first
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, ml[u].x);  // a repeated split leaves it as is
+      const float Mu = Mn == -INFINITY ? 0.f : Mn;
+      const float f = __builtin_amdgcn_exp2f(M - Mu);  // 0 while nothing has been added
+      L *= f;
+      acc *= f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float w = s0 + u < nsplit ? __builtin_amdgcn_exp2f(ml[u].x - Mu) : 0.f;
         L += w * ml[u].y;
         acc += w * o[u];
       }
+      M = Mn;
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;

@@ -269,7 +269,10 @@ def test_plan_info_follows_flags(lib):
     out = [ctypes.c_int32() for _ in range(3)]
     refs = [ctypes.byref(x) for x in out]
     assert lib.tree_attn_plan_info(ctypes.byref(_desc()), *refs) == 0
-    assert out[0].value == 1 and out[1].value == 1            # grid kernel, one split
+    # grid kernel; a 200-token bound over 8 pairs: two splits of 128 tokens
+    assert (out[0].value, out[1].value, out[2].value) == (1, 2, 128)
+    assert lib.tree_attn_plan_info(ctypes.byref(_desc(max_ctx_len=128)), *refs) == 0
+    assert (out[1].value, out[2].value) == (1, 128)            # fits one split
     assert lib.tree_attn_plan_info(ctypes.byref(_desc(flags=4)), *refs) == 0
     assert out[0].value == 2                                  # persistent forced
     assert lib.tree_attn_plan_info(ctypes.byref(_desc(flags=1)), *refs) == 0
@@ -279,6 +282,12 @@ def test_plan_info_follows_flags(lib):
     assert out[1].value > 1 and out[1].value * out[2].value >= 4000
     assert lib.tree_attn_plan_info(ctypes.byref(desc), None, None, None) == 0
     assert lib.tree_attn_plan_info(None, *refs) == -1
+    # one sequence, 32 heads, 1024 tokens: 512 / 32 = 16 splits would fit the
+    # resident slots, but a split holds at least 128 tokens: 8 of 128
+    desc = _desc(batch=1, num_heads=32, num_kv_heads=32, max_ctx_len=1024,
+                 max_blocks_per_seq=68, num_blocks=80, rope_max_pos=1088)
+    assert lib.tree_attn_plan_info(ctypes.byref(desc), *refs) == 0
+    assert (out[0].value, out[1].value, out[2].value) == (1, 8, 128)
 
 
 def test_one_node_trees_take_the_decode_kernel(lib):
@@ -329,7 +338,7 @@ def test_misaligned_tensor_pointers(lib):
 
 
 def test_workspace_size_grows_with_context(lib):
-    a = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=200)))
+    a = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=128)))   # one split
     b = lib.tree_attn_workspace_size(ctypes.byref(_desc(max_ctx_len=4000, max_blocks_per_seq=260,
                                                         rope_max_pos=4064)))
     assert b >= a
