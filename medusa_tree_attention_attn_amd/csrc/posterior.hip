@@ -19,7 +19,11 @@
 namespace ta {
 namespace {
 
-constexpr int kArgThreads = 256;  // threads per logits row
+constexpr int kArgThreads = 256;  // threads per logits row (argmax)
+// Threads per logits row of the entropy pass (16 x 64 rows of 32000 bf16,
+// with two chunks per batch: 18.5 us at 256 threads, 18.8 at 512; with one
+// chunk per batch 19.4, 20.1 and 23.5 at 256, 512 and 1024).
+constexpr int kEntThreads = 256;
 
 struct Best {
   float v;
@@ -39,7 +43,7 @@ __device__ __forceinline__ void take(Best& b, float v, int i) {
 }
 
 // Streams a row of nchunks 16-byte chunks through registers: thread tid
-// takes chunks i * kArgThreads + tid for i = 0, 1, ..., in increasing order,
+// takes chunks i * Op::kThreads + tid for i = 0, 1, ..., in increasing order,
 // in batches of Op::kBatch, with the next batch in flight while one is
 // consumed.  The loads are unconditional (an index past the row reads its
 // last chunk, which the consumer ignores), so the compiler's wait counts
@@ -52,26 +56,27 @@ template <typename Op>
 __device__ __forceinline__ void stream_row(const u32x4* __restrict__ src, int nchunks, int tid,
                                            Op& op) {
   constexpr int kB = Op::kBatch;
-  const int n = (nchunks + kArgThreads - 1) / kArgThreads;  // chunks per thread
+  constexpr int kT = Op::kThreads;  // threads streaming the row
+  const int n = (nchunks + kT - 1) / kT;  // chunks per thread
   const int last = nchunks - 1;
   u32x4 ra[kB], rb[kB];
 #pragma unroll
-  for (int u = 0; u < kB; ++u) ra[u] = __builtin_nontemporal_load(&src[min(u * kArgThreads + tid, last)]);
+  for (int u = 0; u < kB; ++u) ra[u] = __builtin_nontemporal_load(&src[min(u * kT + tid, last)]);
   // Keep batch a's loads ahead of batch b's: the wait for a then leaves b in
   // flight, on the first pass as on every later one.
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < kB; ++u)
-    rb[u] = __builtin_nontemporal_load(&src[min((kB + u) * kArgThreads + tid, last)]);
+    rb[u] = __builtin_nontemporal_load(&src[min((kB + u) * kT + tid, last)]);
   for (int i0 = 0; i0 < n; i0 += 2 * kB) {
     op.batch(ra, i0);
 #pragma unroll
     for (int u = 0; u < kB; ++u)
-      ra[u] = __builtin_nontemporal_load(&src[min((i0 + 2 * kB + u) * kArgThreads + tid, last)]);
+      ra[u] = __builtin_nontemporal_load(&src[min((i0 + 2 * kB + u) * kT + tid, last)]);
     op.batch(rb, i0 + kB);
 #pragma unroll
     for (int u = 0; u < kB; ++u)
-      rb[u] = __builtin_nontemporal_load(&src[min((i0 + 3 * kB + u) * kArgThreads + tid, last)]);
+      rb[u] = __builtin_nontemporal_load(&src[min((i0 + 3 * kB + u) * kT + tid, last)]);
   }
 }
 
@@ -79,6 +84,7 @@ __device__ __forceinline__ void stream_row(const u32x4* __restrict__ src, int nc
 template <typename S>
 struct ArgmaxOp {
   static constexpr int kBatch = 1;
+  static constexpr int kThreads = kArgThreads;
   Best b;
   int nchunks, tid;
   __device__ __forceinline__ void batch(const u32x4 (&x)[kBatch], int i0) {
@@ -202,6 +208,7 @@ __device__ __forceinline__ void add_term(Lse& t, float x, float c) {
 template <typename S>
 struct EntropyOp {
   static constexpr int kBatch = 2;
+  static constexpr int kThreads = kEntThreads;
   Lse a;
   float c;
   int nchunks, tid;
@@ -209,7 +216,7 @@ struct EntropyOp {
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if ((i0 + u) * kArgThreads + tid < nchunks) {
+      if ((i0 + u) * kThreads + tid < nchunks) {
 #pragma unroll
         for (int w = 0; w < 4; ++w)
           mx = sizeof(S) == 2 ? fmaxf(mx, fmaxf(bf16_lo(x[u][w]), bf16_hi(x[u][w])))
@@ -220,7 +227,7 @@ struct EntropyOp {
     Lse t{mx * c, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if ((i0 + u) * kArgThreads + tid < nchunks) {
+      if ((i0 + u) * kThreads + tid < nchunks) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           if (sizeof(S) == 2) {
@@ -237,10 +244,10 @@ struct EntropyOp {
 };
 
 template <typename S>
-__global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __restrict__ logits,
+__global__ __launch_bounds__(kEntThreads) void row_entropy_kernel(const S* __restrict__ logits,
                                                                   int V, float c,
                                                                   float2* __restrict__ stats) {
-  __shared__ Lse s_l[kArgThreads / 64];
+  __shared__ Lse s_l[kEntThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const S* row = logits + (size_t)blockIdx.x * V;
   Lse a{-INFINITY, 0.f, 0.f};
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __res
     stream_row(reinterpret_cast<const u32x4*>(row), V / kPer, tid, op);
     a = op.a;
   } else {
-    for (int i = tid; i < V; i += kArgThreads) {
+    for (int i = tid; i < V; i += kEntThreads) {
       const float x = ld(row, i);
       if (x == -INFINITY) continue;
       Lse t{x * c, 0.f, 0.f};
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(kArgThreads) void row_entropy_kernel(const S* __res
   if (tid == 0) {
     Lse r = s_l[0];
 #pragma unroll
-    for (int w = 1; w < kArgThreads / 64; ++w) merge_lse(r, s_l[w]);
+    for (int w = 1; w < kEntThreads / 64; ++w) merge_lse(r, s_l[w]);
     constexpr float kLn2 = 0.69314718055994531f;
     const float l2z = __log2f(r.z);
     stats[blockIdx.x] = r.z > 0.f ? float2{(r.m + l2z) * kLn2, (l2z - r.s / r.z) * kLn2}
@@ -314,13 +321,13 @@ hipError_t launch_typical_accept(const void* logits, int dtype, int V, int B, in
   const float c = 1.4426950408889634f / temperature;  // log2(e) / temperature
   float2* stats = reinterpret_cast<float2*>(node_stats);
   if (dtype == TA_BF16) {
-    hipLaunchKernelGGL(row_entropy_kernel<uint16_t>, dim3((unsigned)(B * T)), dim3(kArgThreads),
+    hipLaunchKernelGGL(row_entropy_kernel<uint16_t>, dim3((unsigned)(B * T)), dim3(kEntThreads),
                        0, stream, static_cast<const uint16_t*>(logits), V, c, stats);
     hipLaunchKernelGGL(typical_accept_kernel<uint16_t>, dim3((unsigned)B), dim3(64), 0, stream,
                        static_cast<const uint16_t*>(logits), V, T, inv_temp, epsilon, delta,
                        stats, cand_tokens, tree_parent, node_ok, accept_len, accept_path);
   } else {
-    hipLaunchKernelGGL(row_entropy_kernel<float>, dim3((unsigned)(B * T)), dim3(kArgThreads), 0,
+    hipLaunchKernelGGL(row_entropy_kernel<float>, dim3((unsigned)(B * T)), dim3(kEntThreads), 0,
                        stream, static_cast<const float*>(logits), V, c, stats);
     hipLaunchKernelGGL(typical_accept_kernel<float>, dim3((unsigned)B), dim3(64), 0, stream,
                        static_cast<const float*>(logits), V, T, inv_temp, epsilon, delta,
