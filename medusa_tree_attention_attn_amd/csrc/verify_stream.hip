@@ -43,7 +43,9 @@ constexpr int kJStage = 2 * kJKBytes;               // K then V rows (64 KB)
 constexpr int kQBufU4 = 2 * 8 * 64;                 // q fragments of a unit (u32x4 units)
 constexpr int kPagesMax = kMaxSplitTokens / kPage;  // page ids of one split
 constexpr int kAhead = 3;                           // jobs left when the next unit is taken
-constexpr int kNt = 2;  // cache-policy operand of the direct-to-LDS loads: non-temporal (read once)
+// Cache-policy operand of the direct-to-LDS loads: non-temporal (the data is
+// read once).
+constexpr int kNt = 2;
 constexpr int kParkO = 64 * 64;                     // O^T of one wavefront (floats)
 static_assert(2 * kJStage + 2 * kPagesMax * 4 + kQBufU4 * 16 + 4 * 2 * 64 * 4 + 16 <= 163840,
               "LDS budget");
