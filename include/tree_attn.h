@@ -125,8 +125,8 @@ typedef struct tree_attn_desc {
   int32_t flags;              /* enum ta_flags, 0 by default                  */
   int32_t split_tokens;       /* context tokens per split-KV work item of the */
                               /* MFMA kernel, rounded up to a multiple of 64  */
-                              /* and capped at 4096; 0 = chosen from batch,   */
-                              /* heads and max_ctx_len                        */
+                              /* and capped at 8192; 0 = chosen from batch,   */
+                              /* heads and max_ctx_len (never below 128)      */
 } tree_attn_desc;
 
 /* Tree attention (vLLM #1171: several new tokens over a paged KV cache under
