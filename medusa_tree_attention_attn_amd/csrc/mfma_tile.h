@@ -117,6 +117,24 @@ __device__ __forceinline__ void compute_tile(WaveState& st, const u32x4 (&qf)[8]
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
     s = mfma(*reinterpret_cast<const u32x4*>(kp + 32 * ks), qf[ks], s);
+  // The V^T fragments of the PV product do not depend on the probabilities.
+  // In the full-tile mode of the tile loop they are read here, so that their
+  // LDS latency overlaps the softmax (the rescale branch below ends the basic
+  // block, and the scheduler does not move loads across it); the masked
+  // modes read them after the softmax, where their registers are free.
+  v8i16 va[4][2];
+  const char* vp = stage + L.v;
+  auto read_v = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const v4i16 lo = ds_read_tr(vp + (16 * ks) * kVRow + 64 * dt);
+        const v4i16 hi = ds_read_tr(vp + (16 * ks + 8) * kVRow + 64 * dt);
+        va[dt][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  };
+  if constexpr (kMode == kFull) read_v();
   if (kMode != kFull) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -149,17 +167,13 @@ __device__ __forceinline__ void compute_tile(WaveState& st, const u32x4 (&qf)[8]
   }
   st.m = m_new;
   const bf16x8 pk[2] = {__builtin_convertvector(p0, bf16x8), __builtin_convertvector(p1, bf16x8)};
-  const char* vp = stage + L.v;
+  if constexpr (kMode != kFull) read_v();
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const v4i16 lo = ds_read_tr(vp + (16 * ks) * kVRow + 64 * dt);
-      const v4i16 hi = ds_read_tr(vp + (16 * ks + 8) * kVRow + 64 * dt);
-      const v8i16 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ks],
-                                                          st.o[dt], 0, 0, 0);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[dt][ks]),
+                                                          pk[ks], st.o[dt], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
