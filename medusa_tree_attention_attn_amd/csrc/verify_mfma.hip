@@ -224,18 +224,20 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
   }
 }
 
-// Output of an unsplit item.  The th = 0 wavefronts write their normalised
-// rows as bf16 (lane = query column, four consecutive dims per value group)
-// into a row-major tile in LDS; then all four wavefronts store whole
-// 256-byte rows of `out`, 16 bytes per lane, instead of 8-byte pieces of 32
-// rows per instruction.  Rows q >= T are not stored; padding rows are zeros.
+// Output of an unsplit item.  Each wavefront writes its two d-tiles of the
+// normalised rows as bf16 (lane = query column, four consecutive dims per
+// value group) into a row-major tile in LDS; then all four wavefronts store
+// whole 256-byte rows of `out`, 16 bytes per lane, instead of 8-byte pieces
+// of 32 rows per instruction.  Rows q >= T are not stored; padding rows are
+// zeros.
 constexpr int kOutRow = 256 + 16;  // padded: the value-group writes spread over the banks
+template <int d0>
 __device__ __forceinline__ void stage_out(const WaveState& st, char* tile, int q, bool row_real,
                                           int g) {
   const float inv = (row_real && st.l > 0.f) ? 1.0f / st.l : 0.f;
   char* row = tile + q * kOutRow;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = d0; dt < d0 + 2; ++dt)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const f32x4 v4 = {st.o[dt][4 * rb] * inv, st.o[dt][4 * rb + 1] * inv,
@@ -255,6 +257,58 @@ __device__ __forceinline__ void store_out(const char* tile, const VerifyParams& 
                                 (((size_t)b * p.T + row) * p.H + h) * kD + 8 * ch) =
           *reinterpret_cast<const u32x4*>(tile + row * kOutRow + 16 * ch);
   }
+}
+
+// Merge of the two token halves of a query tile, shared by its two
+// wavefronts: wavefront th keeps d-tiles 2th and 2th+1 of O^T.  Each parks
+// the other pair and its (m, l) in a lane-major block of 34 x 64 floats, and
+// after a barrier merges its own pair with the pair its partner parked.  The
+// running sums are combined in one fixed order (th = 0's first), so both
+// wavefronts hold the same l.
+constexpr int kHalfPark = 34 * 64;  // floats per wavefront
+template <int kDOther>
+__device__ __forceinline__ void park_half(const WaveState& st, float* blk, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) blk[(16 * j + r) * 64 + lane] = st.o[kDOther + j][r];
+  blk[32 * 64 + lane] = st.m;
+  blk[33 * 64 + lane] = st.l;
+}
+template <int kTh>
+__device__ __forceinline__ void merge_half(WaveState& st, const float* pblk, int lane) {
+  constexpr int d_own = 2 * kTh;
+  const float m1 = pblk[32 * 64 + lane], l1 = pblk[33 * 64 + lane];
+  const float M = fmaxf(st.m, m1);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  const float w_own = __builtin_amdgcn_exp2f(st.m - Mu);
+  const float w_par = __builtin_amdgcn_exp2f(m1 - Mu);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      st.o[d_own + j][r] = st.o[d_own + j][r] * w_own + pblk[(16 * j + r) * 64 + lane] * w_par;
+  const float la = kTh == 0 ? st.l : l1, wa = kTh == 0 ? w_own : w_par;
+  const float lb = kTh == 0 ? l1 : st.l, wb = kTh == 0 ? w_par : w_own;
+  st.l = la * wa + lb * wb;
+  st.m = M;
+}
+// Split partial of a work item: this wavefront's two d-tiles of O^T; the
+// th = 0 wavefront also writes (m, l).
+template <int d0>
+__device__ __forceinline__ void write_partial_half(const WaveState& st, const VerifyParams& p,
+                                                   int bh, int sp, int q, int T, bool row_real,
+                                                   int g, bool write_ml) {
+  if (!row_real) return;
+  const size_t row = ((size_t)bh * p.splits + sp) * T + q;
+  float* orow = p.ws_o + row * kD;
+#pragma unroll
+  for (int dt = d0; dt < d0 + 2; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * rb + 4 * g) =
+          f32x4{st.o[dt][4 * rb], st.o[dt][4 * rb + 1], st.o[dt][4 * rb + 2], st.o[dt][4 * rb + 3]};
+  if (write_ml && g == 0) p.ws_ml[row] = float2{st.m, st.l};
 }
 
 // Launch slot -> (sequence, head, split).  A (sequence, split) group holds H
@@ -310,7 +364,7 @@ __device__ unsigned long long ta_trace_buf[1 << 16][12];
 
 __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(VerifyParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
-  static_assert(2 * 66 * 64 * sizeof(float) <= 2 * kStageBytes, "merge area");
+  static_assert(4 * kHalfPark * sizeof(float) <= 2 * kStageBytes, "merge area");
   __shared__ int s_pages[kMaxSplitPages];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -462,27 +516,43 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
     }
   }
 
-  // Merge the two token halves of each query tile (wavefront th=1 -> th=0).
+  // Merge the two token halves of each query tile; each wavefront of the
+  // pair finishes two of the four d-tiles.
   __syncthreads();
 #ifdef TA_TRACE
   if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][5] = wall_clock64();
 #endif
-  float* mb = reinterpret_cast<float*>(smem) + qt * kParkFloats;  // [2][66][64]
-  if (active && th == 1) park_state(st, mb, lane);
+  // (th is uniform over a wavefront: each branch indexes the accumulators
+  // with constants.)
+  float* park = reinterpret_cast<float*>(smem);
+  if (active) {
+    if (th == 0)
+      park_half<2>(st, park + (2 * qt) * kHalfPark, lane);
+    else
+      park_half<0>(st, park + (2 * qt + 1) * kHalfPark, lane);
+  }
   __syncthreads();
-  if (th == 0 && active) {
-    merge_state(st, mb, mb[64 * 64 + lane], mb[65 * 64 + lane], lane);
+  if (active) {
+    if (th == 0)
+      merge_half<0>(st, park + (2 * qt + 1) * kHalfPark, lane);
+    else
+      merge_half<1>(st, park + (2 * qt) * kHalfPark, lane);
     st.l += __shfl_xor(st.l, 32);
   }
   if (nsplit == 1) {  // uniform
-    static_assert(2 * kParkFloats * sizeof(float) + kTile * kOutRow <= 2 * kStageBytes,
+    static_assert(4 * kHalfPark * sizeof(float) + kTile * kOutRow <= 2 * kStageBytes,
                   "output tile after the park area");
-    char* tile = smem + 2 * kParkFloats * sizeof(float);
-    if (th == 0) stage_out(st, tile, q, row_real, g);
+    char* tile = smem + 4 * kHalfPark * sizeof(float);
+    if (th == 0)
+      stage_out<0>(st, tile, q, row_real, g);
+    else
+      stage_out<2>(st, tile, q, row_real, g);
     __syncthreads();
     store_out(tile, p, b, h, tid);
   } else if (th == 0) {
-    write_result(st, p, b, h, bh, sp, nsplit, q, T, row_real, g);
+    write_partial_half<0>(st, p, bh, sp, q, T, row_real, g, true);
+  } else {
+    write_partial_half<2>(st, p, bh, sp, q, T, row_real, g, false);
   }
 #ifdef TA_TRACE
   if (tid == 0 && blockIdx.x < (1u << 16)) {
