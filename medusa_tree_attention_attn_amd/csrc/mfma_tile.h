@@ -287,16 +287,6 @@ __device__ __forceinline__ void merge_state(WaveState& st, const float* o1, floa
   st.m = M;
 }
 
-// Write st (O^T rows, m, l) to an LDS block of 66 x 64 floats (lane-major).
-__device__ __forceinline__ void park_state(const WaveState& st, float* blk, int lane) {
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) blk[(dt * 16 + r) * 64 + lane] = st.o[dt][r];
-  blk[64 * 64 + lane] = st.m;
-  blk[65 * 64 + lane] = st.l;
-}
-constexpr int kParkFloats = 66 * 64;
 
 // Write only O^T (64 x 64 floats, lane-major); m and l travel separately.
 __device__ __forceinline__ void park_o(const WaveState& st, float* blk, int lane) {
