@@ -357,10 +357,6 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
   return true;
 }
 
-#ifdef TA_TRACE
-__device__ unsigned long long ta_trace_buf[1 << 16][12];
-#define TA_STAMP(i) do { if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][i] = wall_clock64(); } while (0)
-#endif
 
 __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(VerifyParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
@@ -373,9 +369,6 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   int b, h, sp;
   if (!launch_item(p, blockIdx.x, lane, b, h, sp)) return;
   const int bh = b * p.H + h;
-#ifdef TA_TRACE
-  const unsigned long long trace_t0 = wall_clock64();
-#endif
   const int hk = h / (p.H / p.Hkv);
   const int T = p.T;
   const int q = 32 * qt + r32;
@@ -441,9 +434,6 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int pos_j = ctx + clampi(__shfl(dep, tid >> 2), 0, T - 1);
 
   lds_sync();  // s_pages visible; the q and tree k/v rows may still be in flight
-#ifdef TA_TRACE
-  TA_STAMP(8);
-#endif
   // ---- round trip 2: the (cos, sin) rows and context tile 0; tile 1 follows
   // once q is rotated, and the tree tile is built and computed while it
   // loads.
@@ -473,27 +463,15 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   char* stage1 = smem + kStageBytes;
 
   const LaneOffs L = lane_offsets(lane, th, kKBytes);
-#ifdef TA_TRACE
-  TA_STAMP(9);
-#endif
   // The tree tile goes through stage 1 while context tiles 0 and 1 load.
   if (sp == 0) {
     store_tree_tile(stage1, TR, t_real, tid);
     lds_sync();
-#ifdef TA_TRACE
-    TA_STAMP(10);
-#endif
     if (active) compute_tile<kTreeTile>(st, qf, stage1, L, kTile, anc_q);
   }
-#ifdef TA_TRACE
-  TA_STAMP(11);
-#endif
   auto rows_of = [&](int t) { return min(kTile, c1 - (c0 + kTile * t)); };
   if (n_tiles > 0) store_tile(R0, stage0, rows_of(0), tid);
   lds_sync();  // stage 0 filled, stage 1's tree reads done; tile 1 stays in flight
-#ifdef TA_TRACE
-  TA_STAMP(4);
-#endif
   if (n_tiles > 0) {
     // Every tile but the last is full: one straight-line path, no masking.
     for (int t = 0; t < n_tiles - 1; ++t) {
@@ -519,9 +497,6 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   // Merge the two token halves of each query tile; each wavefront of the
   // pair finishes two of the four d-tiles.
   __syncthreads();
-#ifdef TA_TRACE
-  if (tid == 0 && blockIdx.x < (1u << 16)) ta_trace_buf[blockIdx.x][5] = wall_clock64();
-#endif
   // (th is uniform over a wavefront: each branch indexes the accumulators
   // with constants.)
   float* park = reinterpret_cast<float*>(smem);
@@ -554,16 +529,6 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   } else {
     write_partial_half<2>(st, p, bh, sp, q, T, row_real, g, false);
   }
-#ifdef TA_TRACE
-  if (tid == 0 && blockIdx.x < (1u << 16)) {
-    ta_trace_buf[blockIdx.x][0] = trace_t0;
-    ta_trace_buf[blockIdx.x][1] = wall_clock64();
-    ta_trace_buf[blockIdx.x][2] = __builtin_amdgcn_s_getreg((31 << 11) | 4);
-    ta_trace_buf[blockIdx.x][3] = __builtin_amdgcn_s_getreg((31 << 11) | 20);
-    ta_trace_buf[blockIdx.x][6] = (unsigned long long)b;
-    ta_trace_buf[blockIdx.x][7] = (unsigned long long)h;
-  }
-#endif
 }
 
 // Merge the (m, l, O) partials of every (sequence, head) whose context took
@@ -636,11 +601,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(VerifyParams p) {
 
 }  // namespace
 
-#ifdef TA_TRACE
-extern "C" int ta_trace_fetch(void* host, size_t bytes) {
-  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(ta_trace_buf), bytes);
-}
-#endif
 
 hipError_t launch_verify_mfma(const VerifyParams& p, hipStream_t stream) {
   const long long grid = (long long)p.B * p.H * p.splits;
