@@ -166,8 +166,10 @@ __device__ __forceinline__ bool finish_fetch(Fetch& F, Unit& U, Tree& TRi, const
   TRi.dep = clampi(F.dep, 0, T - 1);
   if (!valid) return false;
 
+  // A page id outside the pool reads pool page 0, as in the grid kernel: its
+  // K and V rows are then finite data, scored like any other token.
   const int npages = (span + kPage - 1) / kPage;
-  if (tid < npages) pages[tid] = (F.blk >= 0 && F.blk < p.num_blocks) ? F.blk : -1;
+  if (tid < npages) pages[tid] = (F.blk >= 0 && F.blk < p.num_blocks) ? F.blk : 0;
   return true;
 }
 
@@ -356,12 +358,6 @@ __device__ __forceinline__ void rotate_tree_job(char* stage, int t_real, int tid
   }
 }
 
-#ifdef TA_TRACE
-// Per-workgroup timeline: [0] start, [1] end, [2] HW_ID, [3] XCC_ID, [4] steps,
-// [5] units, [8 + 4 i + j] wall clock at points j of step i.
-__device__ unsigned long long ts_trace_buf[1024][128];
-#define TS_STAMP(i, v) do { if (threadIdx.x == 0 && blockIdx.x < 1024u && (i) < 128) ts_trace_buf[blockIdx.x][i] = (v); } while (0)
-#endif
 
 __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kJStage];
@@ -415,10 +411,6 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
   reset(st);
   __syncthreads();  // s_next
 
-#ifdef TA_TRACE
-  int trace_step = 0, trace_units = 0;
-  TS_STAMP(0, wall_clock64());
-#endif
   for (;;) {
     // Lane-derived offsets are recomputed every step from an opaque copy of
     // the thread index: hoisted out of the loop they would pin ~190 VGPRs.
@@ -426,9 +418,6 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int q = 32 * qt + (lane & 31);
-#ifdef TA_TRACE
-    TS_STAMP(8 + 4 * trace_step, wall_clock64());
-#endif
     // ---- 1. compute job k of U out of stage(cur).
     if (k >= 0 && active) {
       const char* sg = smem + cur * kJStage;
@@ -443,9 +432,6 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
       }
     }
     const bool u_done = u_live && k == U.n_jobs - 1;
-#ifdef TA_TRACE
-    TS_STAMP(9 + 4 * trace_step, wall_clock64());
-#endif
 
     // ---- 2. next unit: the step before the barrier.
     if (phase == kGrabbed) {
@@ -469,9 +455,6 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
       rotate_tree_job(nxt, r_n ? N.t_real : U.t_real, tid);
       lds_barrier();
     }
-#ifdef TA_TRACE
-    TS_STAMP(10 + 4 * trace_step, wall_clock64());
-#endif
 
     // ---- 4. next unit: the step after the barrier.
     if (phase == kPublished) {
@@ -546,19 +529,12 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
       rk = lk;
       ++lk;
     }
-#ifdef TA_TRACE
-    TS_STAMP(11 + 4 * trace_step, wall_clock64());
-    ++trace_step;
-#endif
 
     // ---- 7. the staged job becomes current; N's first job makes N current.
     if (staged) {
       cur ^= 1;
       k = staged_k;
       if (staged_n) {
-#ifdef TA_TRACE
-        ++trace_units;
-#endif
         U = N;
         TU = TN;
         u_live = true;
@@ -578,13 +554,6 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
     }
   }
 
-#ifdef TA_TRACE
-  TS_STAMP(1, wall_clock64());
-  TS_STAMP(2, __builtin_amdgcn_s_getreg((31 << 11) | 4));
-  TS_STAMP(3, __builtin_amdgcn_s_getreg((31 << 11) | 20));
-  TS_STAMP(4, trace_step);
-  TS_STAMP(5, trace_units);
-#endif
   // The last workgroup out puts the counters back to zero for the next launch.
   if (tid0 == 0) {
     if (atomicAdd(p.ws_ctr + 1, 1u) == (uint32_t)grid - 1u) {
@@ -596,11 +565,6 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
 
 }  // namespace
 
-#ifdef TA_TRACE
-extern "C" int ts_trace_fetch(void* host, size_t bytes) {
-  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(ts_trace_buf), bytes);
-}
-#endif
 
 hipError_t launch_verify_stream(const VerifyParams& p, hipStream_t stream) {
   const long long units = (long long)p.B * p.H * p.splits;

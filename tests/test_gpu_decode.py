@@ -21,13 +21,9 @@ import torch
 
 import oracle
 from synth import make_workload
-from tests._helpers import dev, oracle_verify_rows, pool_bits, verifier
+from tests._helpers import ATOL, check_attention_rows, dev, oracle_verify_rows, pool_bits, verifier
 
 pytestmark = pytest.mark.gpu
-
-ATOL = 1e-2
-RTOL_OUT_ROUNDING = 2.0 ** -8
-
 
 def _run(wl, flags=0):
     d = dev(wl)
@@ -40,16 +36,7 @@ def _run(wl, flags=0):
     return out.float().cpu().numpy(), kernel
 
 
-def _check(got, ref, wl, seqs):
-    real = wl.tree_parent[seqs] != oracle.PAD_PARENT
-    assert np.all(got[~real] == 0.0), "padding rows must be zero"
-    err = np.abs(got - ref)
-    worst = float(err[real].max()) if real.any() else 0.0
-    print(f"  max |gpu - oracle| = {worst:.3e}", flush=True)
-    bound = ATOL + RTOL_OUT_ROUNDING * np.abs(ref)
-    if int(np.min(wl.ctx_lens[seqs])) >= 128:
-        bound = np.full_like(ref, ATOL)
-    assert np.all(err[real] <= bound[real]), float((err / bound)[real].max())
+_check = check_attention_rows
 
 
 CASES = [

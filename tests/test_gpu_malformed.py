@@ -6,9 +6,11 @@ token ids), but every kernel bounds-checks them.  Here each call is given
 such garbage: it must complete, and a valid call made afterwards must still
 match the oracle (the device and the library are unharmed).
 
-Kernels covered: the one-workgroup-per-item tree kernel, the decode kernel,
-acceptance, the fused acceptance + commit, the commit with a garbage path,
-the greedy-token argmax + acceptance and typical acceptance.
+Kernels covered: the three tree kernels (one workgroup per work item, the
+persistent one that takes work items from a counter, and the plain
+one-wavefront-per-node kernel), the decode kernel, acceptance, the fused
+acceptance + commit, the commit with a garbage path, the greedy-token
+argmax + acceptance and typical acceptance.
 """
 import numpy as np
 import pytest
@@ -36,17 +38,19 @@ def _garbage(wl, seed):
     )
 
 
-@pytest.mark.parametrize("name,kw", [
-    ("vicuna7b_b16", dict(batch=5, heads=3, ctx_range=(10, 900))),
-    ("decode_b64", dict(batch=5, heads=3, ctx_range=(10, 900))),
-])
-def test_garbage_device_values_are_contained(name, kw):
+@pytest.mark.parametrize("name,kw,flags", [
+    ("vicuna7b_b16", dict(batch=5, heads=3, ctx_range=(10, 900)), 2),   # grid kernel
+    ("vicuna7b_b16", dict(batch=5, heads=3, ctx_range=(10, 900)), 4),   # persistent kernel
+    ("vicuna7b_b16", dict(batch=5, heads=3, ctx_range=(10, 900)), 1),   # plain kernel
+    ("decode_b64", dict(batch=5, heads=3, ctx_range=(10, 900)), 0),     # decode kernel
+], ids=["grid", "persistent", "simple", "decode"])
+def test_garbage_device_values_are_contained(name, kw, flags):
     wl = make_workload(name, 31, **kw)
     d = dev(wl)
-    tv = verifier(wl, flags=2 if wl.spec.t_max > 1 else 0)  # grid kernel / decode kernel
+    tv = verifier(wl, flags=flags)
     g = _garbage(wl, 31)
     pool = d["kv_pages"].clone()
-    print(f"garbage inputs: {name} {kw}", flush=True)
+    print(f"garbage inputs: {name} {kw} flags={flags}", flush=True)
     for rep in range(2):
         tv.verify(d["q"], d["k_new"], d["v_new"], pool, g["block_table"], g["ctx_lens"],
                   g["tree_parent"], g["tree_depth"])

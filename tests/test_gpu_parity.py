@@ -22,18 +22,10 @@ import torch
 
 import oracle
 from synth import make_workload
-from tests._helpers import dev, oracle_verify_rows, pool_bits, verifier
+from tests._helpers import (ATOL, check_attention_rows, dev, oracle_verify_rows, pool_bits,
+                            verifier)
 
 pytestmark = pytest.mark.gpu
-
-ATOL = 1e-2
-# `out` has q's dtype, so the result is rounded to bf16 after the fp32
-# accumulation: that rounding alone is up to 2^-8 * |out|, which exceeds 1e-2
-# once |out| > 2.56.  With contexts of >= 128 tokens (every preset workload)
-# |out| stays well below 1 and the plain 1e-2 bar is asserted; the edge cases
-# with a handful of keys (empty context) get the rounding term on top.
-RTOL_OUT_ROUNDING = 2.0 ** -8
-
 
 def _verify_gpu(wl, flags=0, max_ctx_len=None, split_tokens=0):
     d = dev(wl)
@@ -44,17 +36,7 @@ def _verify_gpu(wl, flags=0, max_ctx_len=None, split_tokens=0):
     return out.float().cpu().numpy()
 
 
-def _check_rows(got, ref, wl, seqs):
-    real = wl.tree_parent[seqs] != oracle.PAD_PARENT        # [len(seqs)][T]
-    err = np.abs(got - ref)
-    assert np.all(got[~real] == 0.0), "padding rows must be zero"
-    worst = float(err[real].max())
-    print(f"  max |gpu - oracle| = {worst:.3e}", flush=True)
-    if int(np.min(wl.ctx_lens[seqs])) >= 128:
-        assert worst <= ATOL, worst
-    else:
-        bound = ATOL + RTOL_OUT_ROUNDING * np.abs(ref)
-        assert np.all(err[real] <= bound[real]), float((err / bound)[real].max())
+_check_rows = check_attention_rows
 
 
 FULL_CASES = [
@@ -192,18 +174,21 @@ def _sample_seqs(wl, k):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,seed,nseq,heads", [
-    ("vicuna7b_b16", 1, 6, [0, 7, 31]),
-    ("vicuna13b_b8", 0, 3, [0, 19, 39]),
-    ("stress_b64", 0, 8, [0, 13, 31]),
+@pytest.mark.parametrize("name,seed,nseq", [
+    ("vicuna7b_b16", 1, 16),   # every sequence
+    ("vicuna13b_b8", 0, 8),    # every sequence
+    ("stress_b64", 0, 16),     # 16 of 64: longest, shortest, every tree size, random others
 ])
-def test_verify_sampled_full_size(name, seed, nseq, heads):
+def test_verify_sampled_full_size(name, seed, nseq):
+    """Full-size launches (the default kernel choice, as the benchmark runs
+    them), checked on every head of the sampled sequences."""
     wl = make_workload(name, seed)
     print(f"verify full-size {name} seed={seed}", flush=True)
     got = _verify_gpu(wl)
     seqs = _sample_seqs(wl, nseq)
-    ref = oracle_verify_rows(wl, seqs, heads)
-    _check_rows(got[seqs][:, :, heads], ref, wl, seqs)
+    print(f"  checking {len(seqs)} sequences x {wl.spec.heads} heads", flush=True)
+    ref = oracle_verify_rows(wl, seqs)
+    _check_rows(got[seqs], ref, wl, seqs)
 
 
 @pytest.mark.parametrize("kernel", ["grid", "persistent"])
@@ -219,6 +204,26 @@ def test_verify_grouped_query_heads(kernel):
     got = _verify_gpu(wl, flags=KERNEL_FLAGS[kernel])
     ref = oracle_verify_rows(wl, [0, 1])
     _check_rows(got, ref, wl, [0, 1])
+
+
+@pytest.mark.parametrize("kernel", ["grid", "persistent"])
+def test_verify_invalid_page_reads_page_zero(kernel):
+    """A block id outside the pool, inside a context, is never used as an
+    address: the MFMA kernels read pool page 0 for it (its tokens are scored
+    with page 0's K and V), so the result equals the oracle run on the same
+    table with those ids replaced by 0."""
+    import dataclasses
+    wl = make_workload("vicuna7b_b16", 23, batch=3, heads=4, ctx_range=(300, 700))
+    table = wl.block_table.copy()
+    table[0, 3] = wl.num_blocks + 5                        # past the pool
+    table[1, int(wl.ctx_lens[1]) // 16 - 1] = -3           # negative, the last full page
+    table[2, 0] = np.iinfo(np.int32).max
+    bad = dataclasses.replace(wl, block_table=table)
+    fixed = dataclasses.replace(wl, block_table=np.where(
+        (table < 0) | (table >= wl.num_blocks), 0, table).astype(np.int32))
+    got = _verify_gpu(bad, flags=KERNEL_FLAGS[kernel])
+    ref = oracle_verify_rows(fixed, range(3))
+    _check_rows(got, ref, fixed, [0, 1, 2])
 
 
 def test_verify_is_deterministic():
