@@ -66,43 +66,51 @@ __device__ __forceinline__ void store8(float* p, const float (&y)[8]) {
   reinterpret_cast<f32x4*>(p)[1] = f32x4{y[4], y[5], y[6], y[7]};
 }
 
-// Where path slot i of sequence b goes: position ctx_len + i and the page
-// holding it (block_table[b][pos / 16], row pos % 16).  Only ctx_len and the
-// table are read, so callers look the page up while the acceptance is still
-// being decided; the table index is clamped and the id is tested only where
-// the rows are stored (commit_row), so nothing here waits on the lookup.
-struct Dest {
-  int pos, blk;
-  bool in_table;  // pos has a table column and a RoPE row
-};
-__device__ __forceinline__ Dest commit_dest(const CommitParams& p, int b, int i, int ctx_raw) {
-  const int pos = clampi(ctx_raw, 0, p.max_ctx) + i;
-  const int lb = pos / kPage;
-  const int blk = p.block_table[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)];
-  return Dest{pos, blk, lb < p.max_blocks && pos < p.rope_max_pos};
+// ---------------------------------------------------------------------------
+// KV commit, one workgroup per (sequence b, group of kCommitHeads KV heads).
+// The workgroup writes every accepted row of its heads: slot i < accept_len
+// takes path node n_i to position p = ctx_len + i, page
+// block_table[b][p / 16], row p % 16.  The rows of one head split into
+// 16-byte tasks: d/16 K tasks (8 RoPE pairs each: x_k and x_{k+d/2}, rotated
+// at p with the fixed-order fp32 arithmetic and rounded to the pool type) and
+// d*sizeof(S)/16 V tasks (bit copies).  Thread t takes tasks t, t + 256, ...
+// of the flattened (slot, head, task) list; with two heads of head_dim 128 in
+// bf16 a slot holds 48 tasks, so a path of up to five rows is one task per
+// thread.  Every load of a task (table entry, k_new or v_new row, (cos, sin)
+// row) is issued before any is used, and the stores are skipped when the
+// page id is out of range, so a task costs about one memory round trip.
+// ---------------------------------------------------------------------------
+constexpr int kCommitHeads = 2;
+constexpr int kCommitThreads = 256;
+
+// The accepted node at path slot i, given the path as a node bitmask: the
+// nodes of a root path have increasing indices (every parent precedes its
+// children), so the node at depth i is the i-th lowest set bit.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int i) {
+  for (int k = 0; k < i; ++k) m &= m - 1;
+  return m ? __builtin_ctzll(m) : -1;
 }
 
-// Path slot at position d.pos holds node n: write its K/V rows there.  Every
-// row load (k_new, v_new, the (cos, sin) row) is issued before the page id
-// is tested, so the table lookup and the row loads share a round trip; the
-// stores are skipped when the page is out of range.
 template <typename S>
-__device__ __forceinline__ void commit_row(const CommitParams& p, int b, int n, const Dest& d) {
-  const bool ok = d.in_table && d.blk >= 0 && d.blk < p.num_blocks;
-  const int slot = d.pos % kPage;
-  const int D = p.D, half = p.D / 2, groups = half / 8;
-  const S* kn = static_cast<const S*>(p.k_new) + ((size_t)b * p.T + n) * p.Hkv * D;
-  const S* vn = static_cast<const S*>(p.v_new) + ((size_t)b * p.T + n) * p.Hkv * D;
+__device__ __forceinline__ void commit_task(const CommitParams& p, int b, int ctx, int i, int n,
+                                            int hk, int r, int groups) {
+  const int D = p.D, half = D / 2;
+  const int pos = ctx + i;
+  const int lb = pos / kPage;
+  const int blk = p.block_table[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)];
+  const bool ok_pos = lb < p.max_blocks && pos < p.rope_max_pos;
   S* pages = static_cast<S*>(p.kv_pages);
-  const float* cs = p.rope + (size_t)min(d.pos, p.rope_max_pos - 1) * D;
-  for (int c = threadIdx.x; c < p.Hkv * groups; c += blockDim.x) {
-    const int hk = c / groups, k0 = (c % groups) * 8;
+  const size_t row = ((size_t)b * p.T + n) * p.Hkv + hk;
+  if (r < groups) {  // K: pairs k0 .. k0+7 and their partners
+    const int k0 = r * 8;
+    const S* kn = static_cast<const S*>(p.k_new) + row * D;
+    const float* cs = p.rope + (size_t)min(pos, p.rope_max_pos - 1) * D + 2 * k0;
     float x1[8], x2[8], cc[8], ss[8], y1[8], y2[8];
-    load8(kn + (size_t)hk * D + k0, x1);
-    load8(kn + (size_t)hk * D + k0 + half, x2);
+    load8(kn + k0, x1);
+    load8(kn + k0 + half, x2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 t = reinterpret_cast<const f32x4*>(cs + 2 * k0)[j];
+      const f32x4 t = reinterpret_cast<const f32x4*>(cs)[j];
       cc[2 * j] = t[0];
       ss[2 * j] = t[1];
       cc[2 * j + 1] = t[2];
@@ -110,57 +118,67 @@ __device__ __forceinline__ void commit_row(const CommitParams& p, int b, int n, 
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) rope_pair_exact(x1[j], x2[j], cc[j], ss[j], y1[j], y2[j]);
-    if (ok) {
-      S* krow = pages + page_row(d.blk, 0, hk, slot, p.Hkv, D);
+    if (ok_pos && blk >= 0 && blk < p.num_blocks) {
+      S* krow = pages + page_row(blk, 0, hk, pos % kPage, p.Hkv, D);
       store8(krow + k0, y1);
       store8(krow + k0 + half, y2);
     }
+  } else {  // V: one 16-byte chunk, copied bit for bit
+    constexpr int kPer16 = 16 / sizeof(S);
+    const int off = (r - groups) * kPer16;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const S*>(p.v_new) + row * D + off);
+    if (ok_pos && blk >= 0 && blk < p.num_blocks)
+      *reinterpret_cast<u32x4*>(pages + page_row(blk, 1, hk, pos % kPage, p.Hkv, D) + off) = v;
   }
-  constexpr int kPer16 = 16 / sizeof(S);
-  const int row_chunks = D / kPer16;
-  for (int c = threadIdx.x; c < p.Hkv * row_chunks; c += blockDim.x) {
-    const int hk = c / row_chunks, off = (c % row_chunks) * kPer16;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(vn + (size_t)hk * D + off);
-    if (ok) *reinterpret_cast<u32x4*>(pages + page_row(d.blk, 1, hk, slot, p.Hkv, D) + off) = v;
+}
+
+// The rows of path slots [0, len) for this workgroup's heads.  node_of(i)
+// gives the node at slot i (-1 or >= T: nothing is written for that slot).
+template <typename S, typename NodeOf>
+__device__ __forceinline__ void commit_heads(const CommitParams& p, int b, int ctx, int len,
+                                             NodeOf node_of) {
+  const int h0 = blockIdx.x * kCommitHeads;
+  const int nh = min(kCommitHeads, p.Hkv - h0);
+  const int groups = p.D / 16;
+  const int per_head = groups + p.D * (int)sizeof(S) / 16;
+  const int per_slot = nh * per_head;
+  for (int t = threadIdx.x; t < len * per_slot; t += kCommitThreads) {
+    const int i = t / per_slot, rem = t - i * per_slot;
+    const int hh = rem / per_head, r = rem - hh * per_head;
+    const int n = node_of(i);
+    if (n < 0 || n >= p.T) continue;
+    commit_task<S>(p, b, ctx, i, n, h0 + hh, r, groups);
   }
 }
 
 template <typename S>
-__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
-  const int i = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams p) {
+  const int b = blockIdx.y;
   const int len = p.accept_len[b];
-  const int n = p.accept_path[(size_t)b * p.T + i];
-  const Dest d = commit_dest(p, b, i, p.ctx_lens[b]);
-  if (i >= len || len > p.T || n < 0 || n >= p.T) return;
-  commit_row<S>(p, b, n, d);
+  const int ctx = clampi(p.ctx_lens[b], 0, p.max_ctx);
+  if (len <= 0 || len > p.T) return;  // uniform
+  const int32_t* path = p.accept_path + (size_t)b * p.T;
+  commit_heads<S>(p, b, ctx, len, [&](int i) { return path[i]; });
 }
 
-// Acceptance and commit in one launch: one workgroup per (path slot i,
-// sequence b).  Every wavefront evaluates the sequence's tree (each gets the
-// same answer; the tree rows are L2 hits after the first), so no LDS or
-// barrier is needed; the slot's page is looked up meanwhile.  The workgroup
-// of slot 0 publishes accept_len/accept_path, and each workgroup whose slot
-// is on the accepted path writes that row.  Same results as accept_kernel
+// Acceptance and commit in one launch: one workgroup per (sequence, group of
+// KV heads).  Every wavefront evaluates the sequence's tree (each gets the
+// same answer; no LDS or barrier is needed), the first workgroup of each
+// sequence publishes accept_len / accept_path, and then every workgroup
+// writes the accepted rows of its heads.  Same results as accept_kernel
 // followed by commit_kernel.
 template <typename S>
-__global__ __launch_bounds__(256) void accept_commit_kernel(CommitParams p,
-                                                            const int32_t* __restrict__ node_argmax,
-                                                            const int32_t* __restrict__ cand_tokens,
-                                                            const int32_t* __restrict__ tree_parent,
-                                                            int32_t* __restrict__ accept_len,
-                                                            int32_t* __restrict__ accept_path) {
-  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  // Round trip 1: the tree rows and ctx_len; then the slot's table entry,
-  // issued before the rows are used.
+__global__ __launch_bounds__(kCommitThreads) void accept_commit_kernel(
+    CommitParams p, const int32_t* __restrict__ node_argmax,
+    const int32_t* __restrict__ cand_tokens, const int32_t* __restrict__ tree_parent,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_path) {
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  // One round trip: the tree rows and ctx_len.
   const AcceptRows rows = load_accept_rows(node_argmax, cand_tokens, tree_parent, b, p.T, lane);
-  const int ctx_raw = p.ctx_lens[b];
-  __builtin_amdgcn_sched_barrier(0);
-  const Dest d = commit_dest(p, b, i, ctx_raw);
-  __builtin_amdgcn_sched_barrier(0);
+  const int ctx = clampi(p.ctx_lens[b], 0, p.max_ctx);
   const Acceptance a = accept_rows(rows, p.T, lane);
-  if (i == 0 && tid < 64) write_acceptance(a, accept_len, accept_path, b, p.T, lane);
-  const uint64_t at_i = __ballot(a.in_tree && ((a.path >> lane) & 1ull) && a.depth == i);
-  if (at_i != 0ull) commit_row<S>(p, b, __builtin_ctzll(at_i), d);
+  if (blockIdx.x == 0 && threadIdx.x < 64) write_acceptance(a, accept_len, accept_path, b, p.T, lane);
+  commit_heads<S>(p, b, ctx, a.len, [&](int i) { return nth_set_bit(a.path, i); });
 }
 
 // (cos, sin) of pos * base^(-2k/d): angle in fp64, one rounding to fp32.
@@ -194,11 +212,11 @@ hipError_t launch_accept(const int32_t* node_argmax, const int32_t* cand_tokens,
 }
 
 hipError_t launch_commit(const CommitParams& p, int dtype, hipStream_t stream) {
-  dim3 grid(p.T, p.B);
+  dim3 grid((p.Hkv + kCommitHeads - 1) / kCommitHeads, p.B);
   if (dtype == TA_BF16)
-    hipLaunchKernelGGL(commit_kernel<uint16_t>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(commit_kernel<uint16_t>, grid, dim3(kCommitThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(commit_kernel<float>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(commit_kernel<float>, grid, dim3(kCommitThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -206,12 +224,12 @@ hipError_t launch_accept_commit(const CommitParams& p, const int32_t* node_argma
                                 const int32_t* cand_tokens, const int32_t* tree_parent,
                                 int32_t* accept_len, int32_t* accept_path, int dtype,
                                 hipStream_t stream) {
-  dim3 grid(p.T, p.B);
+  dim3 grid((p.Hkv + kCommitHeads - 1) / kCommitHeads, p.B);
   if (dtype == TA_BF16)
-    hipLaunchKernelGGL(accept_commit_kernel<uint16_t>, grid, dim3(256), 0, stream, p, node_argmax,
+    hipLaunchKernelGGL(accept_commit_kernel<uint16_t>, grid, dim3(kCommitThreads), 0, stream, p, node_argmax,
                        cand_tokens, tree_parent, accept_len, accept_path);
   else
-    hipLaunchKernelGGL(accept_commit_kernel<float>, grid, dim3(256), 0, stream, p, node_argmax,
+    hipLaunchKernelGGL(accept_commit_kernel<float>, grid, dim3(kCommitThreads), 0, stream, p, node_argmax,
                        cand_tokens, tree_parent, accept_len, accept_path);
   return hipGetLastError();
 }
