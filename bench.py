@@ -154,33 +154,78 @@ def _i32(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
 
-def _oracle_parity(wl, out, L, P, pool_after, nseq=4):
-    """(cpu_baseline leg) Outputs of the timed run against the CPU oracle:
-    acceptance bit-exact for the whole batch; attention within 1e-2 on
-    sampled sequences (all heads); committed rows bit-exact on those
-    sequences' touched pages."""
+def _host_threads() -> int:
+    """CPUs this process may run on (its affinity mask)."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_heads(wl, seqs, threads):
+    """Oracle attention [len(seqs)][T][H][d] of the given sequences, every
+    head: the independent (sequence, head) calls of oracle.verify_head spread
+    over `threads` threads, each with a one-thread BLAS.  Each sequence is
+    handed over as a sub-problem holding only the pages it references."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
-    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
-    ok_accept = np.array_equal(L, Lr) and np.array_equal(P, Pr)
-    order = np.argsort(wl.ctx_lens)
-    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]),
-                   int(order[len(order) // 3])})[:nseq]
+    from threadpoolctl import threadpool_limits
     f = lambda t: t.to(torch.float32).numpy()
-    worst = 0.0
+    subs = []
     for b in seqs:
         table = wl.block_table[[b]]
         used = np.unique(table[table >= 0])
         remap = -np.ones(wl.num_blocks, dtype=np.int64)
         remap[used] = np.arange(len(used))
         t2 = np.where(table >= 0, remap[np.maximum(table, 0)], -1).astype(np.int32)
-        sub_pool = f(wl.kv_pages.index_select(0, torch.from_numpy(used)))
-        q, kn, vn = f(wl.q[[b]]), f(wl.k_new[[b]]), f(wl.v_new[[b]])
-        real = wl.tree_parent[b] != oracle.PAD_PARENT
-        for h in range(wl.spec.heads):
-            ref = oracle.verify_head(q, kn, vn, sub_pool, t2, wl.ctx_lens[[b]],
-                                     wl.tree_parent[[b]], wl.tree_depth[[b]], 0, h)
-            worst = max(worst, float(np.abs(out[b, :, h].float().numpy() - ref)[real].max()))
-    # commit: the pages holding the accepted rows of the sampled sequences
+        subs.append((f(wl.q[[b]]), f(wl.k_new[[b]]), f(wl.v_new[[b]]),
+                     f(wl.kv_pages.index_select(0, torch.from_numpy(used))), t2,
+                     wl.ctx_lens[[b]], wl.tree_parent[[b]], wl.tree_depth[[b]]))
+    H, T, d = wl.spec.heads, wl.spec.t_max, wl.spec.head_dim
+    out = np.zeros((len(seqs), T, H, d))
+
+    def one(job):
+        i, h = job
+        out[i, :, h] = oracle.verify_head(*subs[i], 0, h)
+
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, [(i, h) for i in range(len(seqs)) for h in range(H)]))
+    return out
+
+
+def _oracle_parity(wl, out, L, P, pool_after):
+    """(cpu_baseline leg) Outputs of the timed run against the CPU oracle,
+    for every sequence of the batch: acceptance bit-exact; attention within
+    max-abs 1e-2 on every head of every node; the pages holding the
+    committed rows bit-exact."""
+    import oracle
+    Lr, Pr = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
+    ok_accept = np.array_equal(L, Lr) and np.array_equal(P, Pr)
+    seqs = list(range(wl.spec.batch))
+    ref = _oracle_heads(wl, seqs, min(8, _host_threads()))
+    real = wl.tree_parent != oracle.PAD_PARENT
+    worst = float(np.abs(out.float().numpy() - ref)[real].max())
+    # commit: the pages holding the accepted rows
     rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
     ok_commit = True
     for b in seqs:
@@ -189,21 +234,20 @@ def _oracle_parity(wl, out, L, P, pool_after, nseq=4):
         sub = wl.kv_pages.index_select(0, torch.tensor(pages))
         remap = {p: k for k, p in enumerate(pages)}
         t2 = np.array([[remap.get(int(x), -1) for x in wl.block_table[b]]], dtype=np.int32)
-        ref = oracle.commit(wl.k_new[[b]], wl.v_new[[b]], Lr[[b]], Pr[[b]], sub, t2,
-                            wl.ctx_lens[[b]], rope)
+        ref_pool = oracle.commit(wl.k_new[[b]], wl.v_new[[b]], Lr[[b]], Pr[[b]], sub, t2,
+                                 wl.ctx_lens[[b]], rope)
         got = pool_after.index_select(0, torch.tensor(pages))
-        ok_commit &= torch.equal(got.view(torch.int16), ref.view(torch.int16))
+        ok_commit &= torch.equal(got.view(torch.int16), ref_pool.view(torch.int16))
     return dict(accept_bit_exact=bool(ok_accept), commit_bit_exact=bool(ok_commit),
-                attn_max_abs_err=worst, sampled_sequences=seqs,
+                attn_max_abs_err=worst, checked_sequences=len(seqs),
                 ok=bool(ok_accept and ok_commit and worst <= 1e-2))
 
 
 def cpu_baseline_leg(wl, timed, posterior_out):
-    """The CPU oracle's leg of the benchmark: its results check the outputs
-    of the timed GPU run (and of the greedy-token measurement), then the
-    oracle as it stands is timed on one full step of this workload on one
-    host thread (BLAS limited to 1 thread), scaled to tree-tokens/s.
-    Returns (parity, baseline)."""
+    """The CPU oracle's leg of the benchmark, first half: its results check
+    the outputs of the timed GPU run (and of the greedy-token measurement).
+    The oracle's own timing runs in cpu_baseline_worker.  Returns the parity
+    record."""
     import oracle
     parity = _oracle_parity(wl, *timed)
     if posterior_out is not None:
@@ -222,7 +266,7 @@ def cpu_baseline_leg(wl, timed, posterior_out):
                                               and np.array_equal(Dc, Dcr))
         parity["ok"] = (parity["ok"] and parity["posterior_bit_exact"]
                         and parity["typical"]["ok"] and parity["candidates_bit_exact"])
-    return parity, _oracle_timing(wl)
+    return parity
 
 
 def _typical_parity(wl, logits, S, OK, L, P):
@@ -264,29 +308,103 @@ def _typical_parity(wl, logits, S, OK, L, P):
                         np.abs(H).max() and ok_nodes and ok_path and ok_oracle_path))
 
 
-def _oracle_timing(wl):
+_ORACLE_ARGS = None  # the workload's arrays, inherited by the oracle's worker processes
+
+
+def _oracle_pair(job):
+    """One (sequence, head) of the oracle's attention, in a worker process."""
     import oracle
+    b, h = job
+    return oracle.verify_head(*_ORACLE_ARGS, b, h)
+
+
+def _oracle_timing(wl):
+    """The oracle as it stands, timed on one full step of the workload on
+    every CPU of this process's affinity mask: oracle.verify_head of every
+    (sequence, head) pair over a pool of that many forked processes (each
+    with a one-thread BLAS), then the acceptance walk and the commit.  One
+    untimed step, then the median of three timed steps.  `cpu_util` is the
+    CPU time of this process and its workers over the wall time of the timed
+    steps: the cores actually kept busy.  Runs in a process that never
+    touches the GPU (see cpu_baseline_worker)."""
+    import multiprocessing as mp
+
+    import oracle
+    import psutil
     from threadpoolctl import threadpool_limits
+    global _ORACLE_ARGS
+    threads = _host_threads()
     f = lambda t: t.to(torch.float32).numpy()
-    q, kn, vn, pool = f(wl.q), f(wl.k_new), f(wl.v_new), f(wl.kv_pages)
+    _ORACLE_ARGS = (f(wl.q), f(wl.k_new), f(wl.v_new), f(wl.kv_pages), wl.block_table,
+                    wl.ctx_lens, wl.tree_parent, wl.tree_depth)
     rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
-    reps, dt = 0, 0.0
-    with threadpool_limits(1):
-        while reps < 4 and (reps == 0 or dt < 10.0):
-            t0 = time.perf_counter()
-            oracle.verify(q, kn, vn, pool, wl.block_table, wl.ctx_lens, wl.tree_parent,
-                          wl.tree_depth)
+    jobs = [(b, h) for b in range(wl.spec.batch) for h in range(wl.spec.heads)]
+    me = psutil.Process()
+
+    def cpu_seconds():
+        procs = [me] + me.children(recursive=True)
+        t = 0.0
+        for p in procs:
+            try:
+                c = p.cpu_times()
+                t += c.user + c.system
+            except psutil.Error:
+                pass
+        return t
+
+    with threadpool_limits(1), mp.get_context("fork").Pool(threads) as pool:
+        def step():
+            pool.map(_oracle_pair, jobs, chunksize=max(1, len(jobs) // (4 * threads)))
             L, P = oracle.accept_greedy(wl.node_argmax, wl.cand_tokens, wl.tree_parent)
             oracle.commit(wl.k_new, wl.v_new, L, P, wl.kv_pages, wl.block_table, wl.ctx_lens,
                           rope)
-            dt += time.perf_counter() - t0
-            reps += 1
-    return dict(value=round(reps * wl.tree_tokens / dt, 2), unit="tree-tokens/s", cores=1,
-                kind="oracle",
-                sample=f"{reps} full step(s) of the workload (verify of all {wl.spec.batch}x"
-                       f"{wl.spec.heads} (sequence, head) pairs, acceptance, commit), "
-                       f"seed {wl.seed}, {dt:.1f} s on 1 thread",
+
+        step()  # untimed
+        times, cpu = [], 0.0
+        for _ in range(3):
+            c0, t0 = cpu_seconds(), time.perf_counter()
+            step()
+            times.append(time.perf_counter() - t0)
+            cpu += cpu_seconds() - c0
+    dt = float(np.median(times))
+    return dict(value=round(wl.tree_tokens / dt, 2), unit="tree-tokens/s", cores=threads,
+                kind="oracle", cpu_model=_cpu_model(),
+                cpu_util=round(cpu / sum(times), 2),
+                sample=f"full steps of the workload (oracle.verify_head of all {wl.spec.batch}x"
+                       f"{wl.spec.heads} (sequence, head) pairs over {threads} processes, "
+                       f"acceptance, commit), seed {wl.seed}: 1 untimed + median of 3 timed "
+                       f"steps ({', '.join(f'{t:.2f}' for t in times)} s)",
                 seconds=dt)
+
+
+def cpu_baseline_worker(workload: str, seed: int):
+    """The oracle timing in a process of its own, started before the
+    benchmark touches the GPU (so its worker processes are forked from a
+    process without GPU state).  It waits for a line on stdin, sent once the
+    GPU measurements are done, so the two never compete for the host; then
+    it prints the timing as one JSON line."""
+    from synth import make_workload
+    if not sys.stdin.readline():
+        return
+    res = _oracle_timing(make_workload(workload, seed))
+    print(json.dumps(res), flush=True)
+
+
+def start_cpu_baseline_worker(workload: str, seed: int):
+    import subprocess
+    return subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker",
+                             "--workload", workload, "--seed", str(seed)],
+                            stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True)
+
+
+def finish_cpu_baseline_worker(proc, log):
+    out, _ = proc.communicate("go\n", timeout=900)
+    if proc.returncode != 0:
+        raise SystemExit(f"oracle timing process failed (exit {proc.returncode})")
+    res = json.loads(out.strip().splitlines()[-1])
+    log(f"cpu baseline: {res}")
+    res.pop("seconds", None)
+    return res
 
 
 def _prewarm(fn, ms):
@@ -343,6 +461,33 @@ def time_calls(fn, n_inputs, reps, outputs, prewarm_ms=100.0):
         gpu.append(a.elapsed_time(b) * 1e3 / reps)
     del g
     return round(eager, 2), round(min(gpu), 2)
+
+
+def read_ceiling(dev, prewarm_ms, reps=20):
+    """The device's read-stream rate: tree_attn_stream_read (16-byte
+    non-temporal loads, the KV stream's width and policy) over alternating
+    halves of a 2 GiB buffer, so each call reads 1 GiB that the 256 MB
+    Infinity Cache cannot hold; HIP events around `reps` back-to-back calls
+    after a pre-warm."""
+    from medusa_tree_attention_attn_amd import tree_attn_stream_read
+    half = 1 << 30
+    buf = torch.ones(2 * half, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    parts = (buf[:half], buf[half:])
+    fn = lambda k: tree_attn_stream_read(parts[k % 2], sink)
+    _prewarm(fn, prewarm_ms)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(reps):
+        fn(k)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del buf, parts
+    gbs = half / (us * 1e-6) / 1e9
+    return {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "probe": f"tree_attn_stream_read: 1 GiB contiguous per call, one workgroup per CU, 16-byte non-temporal "
+                     f"loads, {reps} calls, {us:.1f} us each"}
 
 
 def posterior_bench(wl, tv, dev, seed, log, reps=50):
@@ -433,6 +578,7 @@ def main():
                          "clocks ramp up over the first tens of milliseconds of load")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain 512 MiB device copies (for counter scaling)")
+    ap.add_argument("--cpu-baseline-worker", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the verify kernel's traffic record from two rocprofv3 "
                          "counter-collection CSVs of this script, then exit (no GPU used)")
@@ -440,11 +586,17 @@ def main():
     if args.traffic_record:
         write_traffic_record(*args.traffic_record, args.workload, args.seed)
         return
+    if args.cpu_baseline_worker:
+        cpu_baseline_worker(args.workload, args.seed)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the tree-verify step shards by sequence or head with no exchange; "
               "multi-GPU runs are not part of it)", file=sys.stderr)
         sys.exit(2)
+    # The oracle's timing process starts before anything touches the GPU.
+    cpu_worker = None if args.no_cpu_baseline else start_cpu_baseline_worker(args.workload,
+                                                                             args.seed)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     from medusa_tree_attention_attn_amd import TreeVerifier
@@ -582,6 +734,8 @@ def main():
     # kernel is shorter than the Python call).
     ac_gpu = None if args.separate_accept_commit else \
         time_calls(accept_commit, copies, nv, [L, P])[1]
+    ceiling = read_ceiling(dev, args.prewarm_ms)
+    log(f"read ceiling: {ceiling}")
     # restore the outputs of the step loop's last step for the parity check
     step(args.warmup + args.steps - 1)
     torch.cuda.synchronize()
@@ -595,12 +749,11 @@ def main():
     chk = {"checked": False, "why": "--no-cpu-baseline: the oracle leg did not run"}
     if not args.no_cpu_baseline:
         last = sets[(args.warmup + args.steps - 1) % copies]
-        chk, cpu = cpu_baseline_leg(
+        chk = cpu_baseline_leg(
             wl, (last["out"].cpu(), L.cpu().numpy(), P.cpu().numpy(), last["pool"].cpu()),
             posterior_out)
         log(f"parity of timed outputs: {chk}")
-        log(f"cpu baseline: {cpu}")
-        cpu.pop("seconds", None)
+        cpu = finish_cpu_baseline_worker(cpu_worker, log)
         if not chk["ok"]:
             print(json.dumps({"metric": "verified tree-tokens/s", "error": "parity failed",
                               "parity": chk}))
@@ -647,6 +800,8 @@ def main():
                         if args.seed == 0 and args.split_tokens == 0 else None),
             "bytes_per_launch": nbytes["verify"],
             "avg_launch_us": round(v_avg * 1e3, 2),
+            "ceiling": ceiling,
+            "frac_of_ceiling": round(achieved / ceiling["GB/s"], 4),
         },
         "ms_per_step_graph": (round(ms_per_step_graph, 5) if ms_per_step_graph else None),
         "step_hbm_gbs": round(nbytes["step"] / (ms_per_step * 1e-3) / 1e9, 1),
@@ -654,7 +809,7 @@ def main():
                         ("accept, commit" if args.separate_accept_commit else "accept_commit"):
                             round(ac_avg * 1e3, 2),
                         "accept_commit_graph": ac_gpu},
-        "parity": {k: v for k, v in chk.items() if k not in ("ok", "sampled_sequences")},
+        "parity": {k: v for k, v in chk.items() if k != "ok"},
         "posterior": posterior,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

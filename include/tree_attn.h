@@ -321,6 +321,17 @@ int tree_attn_workspace_init(const tree_attn_desc* desc);
 int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* table,
                          void* stream);
 
+/* Read-bandwidth probe (measurement only; no step of the method calls it).
+ * Streams the first bytes/16*16 bytes of the device buffer src with the load
+ * width (16 bytes per lane) and cache policy (non-temporal) of the
+ * tree-verify kernels' KV stream, and XORs them into the device word *sink
+ * (4-byte aligned; its value is meaningless, it only keeps the loads live).
+ * Timing this call on a buffer larger than the 256 MB Infinity Cache gives
+ * the rate at which the device at hand streams a read-only buffer: the
+ * practical ceiling beside the 8 TB/s nominal peak.  src 16-byte aligned.
+ * Errors: TA_ERR_NULL_POINTER, TA_ERR_ALIGNMENT, TA_ERR_LAUNCH. */
+int tree_attn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static description of a status code. */
 const char* tree_attn_strerror(int status);
 

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     tree_argmax_accept,
     tree_attn_plan_info,
     tree_attn_rope_table,
+    tree_attn_stream_read,
     tree_attn_strerror,
     tree_attn_verify,
     tree_attn_workspace_init,

@@ -39,7 +39,7 @@ EXPORTED = (
     "tree_vocab_argmax", "tree_argmax_accept", "tree_accept_typical", "tree_medusa_tree",
     "tree_medusa_candidates",
     "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_plan_info", "tree_attn_rope_table",
-    "tree_attn_strerror",
+    "tree_attn_stream_read", "tree_attn_strerror",
 )
 
 
@@ -106,6 +106,7 @@ def load() -> ctypes.CDLL:
         "tree_attn_plan_info": (ctypes.c_int, [D, P, P, P]),
         "tree_attn_rope_table": (ctypes.c_int, [ctypes.c_int32, ctypes.c_float,
                                                 ctypes.c_int32, P, P]),
+        "tree_attn_stream_read": (ctypes.c_int, [P, ctypes.c_size_t, P, P]),
         "tree_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -370,6 +371,23 @@ def tree_attn_rope_table(head_dim, base, max_pos, table, stream=None):
         _expect(table, (max_pos, head_dim // 2, 2), torch.float32, "rope table")
     rc = load().tree_attn_rope_table(int(head_dim), float(base), int(max_pos), _ptr(table), stream)
     _check(rc, "tree_attn_rope_table")
+
+
+def tree_attn_stream_read(src, sink, nbytes=None):
+    """Read-bandwidth probe: stream the device tensor src (its first nbytes,
+    default all of it) with the KV stream's loads; sink is an int32 device
+    tensor of at least one element.  Enqueued on torch's current stream."""
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    if not (isinstance(sink, torch.Tensor) and sink.is_cuda and sink.dtype == torch.int32
+            and sink.numel() >= 1):
+        raise ValueError("sink must be an int32 device tensor")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if n > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds the tensor")
+    rc = load().tree_attn_stream_read(_ptr(src), n, _ptr(sink),
+                                      current_stream_handle(src.device))
+    _check(rc, "tree_attn_stream_read")
 
 
 def tree_attn_strerror(code: int) -> str:

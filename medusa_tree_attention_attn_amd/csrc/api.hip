@@ -362,6 +362,13 @@ int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* t
                                      static_cast<hipStream_t>(stream)));
 }
 
+int tree_attn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return TA_ERR_NULL_POINTER;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return TA_ERR_ALIGNMENT;
+  return status_of(launch_stream_read(src, bytes, sink, device_cu_count(),
+                                      static_cast<hipStream_t>(stream)));
+}
+
 const char* tree_attn_strerror(int status) {
   switch (status) {
     case TA_OK: return "ok";

@@ -78,4 +78,10 @@ hipError_t launch_rope_table(int head_dim, float base, int max_pos, float* table
 
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
 
+// Read-bandwidth probe: streams bytes (a multiple of 16 is read; the rest is
+// ignored) from src with 16-byte non-temporal loads and XORs them into
+// *sink.  Measurement only.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_cu,
+                              hipStream_t stream);
+
 }  // namespace ta
