@@ -155,6 +155,29 @@ int tree_attn_verify(const tree_attn_desc* desc, const void* q, const void* k_ne
                      const int32_t* tree_parent, const int32_t* tree_depth,
                      void* out);
 
+/* Allocation-free tree_attn_verify, for callers that cannot allocate device
+ * memory or hand the library a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and kernels as tree_attn_verify, except that desc->workspace and
+ * desc->workspace_bytes are ignored: the split-KV partials and the
+ * persistent kernel's work counters live in a static device array of 32 MiB
+ * that the library holds on every device it runs on until the process ends.
+ * The first call on a device resolves the array's address there and zeroes
+ * its 256 bytes of counters with a fill kernel on desc->stream; every call
+ * leaves the counters at zero again.  No call allocates (no hipMalloc,
+ * hipFree or allocating library routine).  All calls on one device share its
+ * array, which keeps the last call's contents: calls that overlap on one
+ * device (concurrent streams or host threads) race and must not be issued.
+ * Errors: those of tree_attn_verify; TA_ERR_WORKSPACE when the plan for the
+ * descriptor needs more than 32 MiB (tree_attn_workspace_size(desc) > 32 MiB:
+ * long contexts cut into many splits); TA_ERR_LAUNCH when the array cannot
+ * be resolved on the current device. */
+int tree_attn_verify_noalloc(const tree_attn_desc* desc, const void* q, const void* k_new,
+                             const void* v_new, const void* kv_pages,
+                             const int32_t* block_table, const int32_t* ctx_lens,
+                             const int32_t* tree_parent, const int32_t* tree_depth,
+                             void* out);
+
 /* Greedy acceptance (LMDeploy #1231 evaluate_posterior at temperature 0).
  * Node c (c >= 1) matches iff cand_tokens[b][c] == node_argmax[b][parent(c)];
  * a node is accepted iff every edge on its root path matches.  The end node

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     tree_attn_stream_read,
     tree_attn_strerror,
     tree_attn_verify,
+    tree_attn_verify_noalloc,
     tree_attn_workspace_init,
     tree_attn_workspace_size,
     tree_medusa_candidates,

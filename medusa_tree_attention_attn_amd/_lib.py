@@ -35,7 +35,7 @@ STATUS = {
     -13: "TA_ERR_CHOICES",
 }
 EXPORTED = (
-    "tree_attn_verify", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
+    "tree_attn_verify", "tree_attn_verify_noalloc", "tree_accept_greedy", "kv_commit_path", "tree_accept_commit",
     "tree_vocab_argmax", "tree_argmax_accept", "tree_accept_typical", "tree_medusa_tree",
     "tree_medusa_candidates",
     "tree_attn_workspace_size", "tree_attn_workspace_init", "tree_attn_plan_info", "tree_attn_rope_table",
@@ -88,6 +88,7 @@ def load() -> ctypes.CDLL:
     D = ctypes.POINTER(TreeAttnDesc)
     sig = {
         "tree_attn_verify": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
+        "tree_attn_verify_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P]),
         "tree_accept_greedy": (ctypes.c_int, [D, P, P, P, P, P]),
         "kv_commit_path": (ctypes.c_int, [D, P, P, P, P, P, P, P]),
         "tree_accept_commit": (ctypes.c_int, [D, P, P, P, P, P, P, P, P, P, P]),
@@ -197,6 +198,27 @@ def tree_attn_verify(desc, q, k_new, v_new, kv_pages, block_table, ctx_lens, tre
                                  _ptr(kv_pages), _ptr(block_table), _ptr(ctx_lens),
                                  _ptr(tree_parent), _ptr(tree_depth), _ptr(out))
     _check(rc, "tree_attn_verify")
+
+
+def tree_attn_verify_noalloc(desc, q, k_new, v_new, kv_pages, block_table, ctx_lens,
+                             tree_parent, tree_depth, out):
+    """tree_attn_verify with the library's static device workspace instead of
+    desc.workspace (no allocation in the call)."""
+    B, T, H, Hkv, d = desc.batch, desc.t_max, desc.num_heads, desc.num_kv_heads, desc.head_dim
+    dt = _dtype_of(desc)
+    _expect(q, (B, T, H, d), dt, "q")
+    _expect(k_new, (B, T, Hkv, d), dt, "k_new")
+    _expect(v_new, (B, T, Hkv, d), dt, "v_new")
+    _expect(kv_pages, (desc.num_blocks, 2, Hkv, 16, d), dt, "kv_pages")
+    _expect(block_table, (B, desc.max_blocks_per_seq), torch.int32, "block_table")
+    _expect(ctx_lens, (B,), torch.int32, "ctx_lens")
+    _expect(tree_parent, (B, T), torch.int32, "tree_parent")
+    _expect(tree_depth, (B, T), torch.int32, "tree_depth")
+    _expect(out, (B, T, H, d), dt, "out")
+    rc = load().tree_attn_verify_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                         _ptr(kv_pages), _ptr(block_table), _ptr(ctx_lens),
+                                         _ptr(tree_parent), _ptr(tree_depth), _ptr(out))
+    _check(rc, "tree_attn_verify_noalloc")
 
 
 def tree_accept_greedy(desc, node_argmax, cand_tokens, tree_parent, accept_len, accept_path):

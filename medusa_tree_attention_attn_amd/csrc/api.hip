@@ -1,11 +1,15 @@
 // C ABI of the tree-verify library: host-side validation, split planning and
-// dispatch.  No allocation, no device->host synchronisation, no global state.
+// dispatch.  No allocation and no device->host synchronisation.  The only
+// global state is the static device workspace of tree_attn_verify_noalloc
+// and its per-device address.
 #include <math.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <map>
+#include <mutex>
 #include <vector>
 
 #include "launch.h"
@@ -13,7 +17,17 @@
 
 using namespace ta;
 
+// Workspace of tree_attn_verify_noalloc: one file-scope device array, which
+// every GPU the library runs on holds (at its own address) until the process
+// ends.  In host code `scratch` only names the symbol: its device address on
+// a given device comes from hipGetSymbolAddress (scratch_on_current_device
+// below), and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
 
 int check_common(const tree_attn_desc* d) {
   if (!d) return TA_ERR_NULL_POINTER;
@@ -80,21 +94,28 @@ int tree_attn_workspace_init(const tree_attn_desc* d) {
                                     static_cast<hipStream_t>(d->stream)));
 }
 
-int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
-                     const void* v_new, const void* kv_pages, const int32_t* block_table,
-                     const int32_t* ctx_lens, const int32_t* tree_parent,
-                     const int32_t* tree_depth, void* out) {
+}  // extern "C"
+
+namespace {
+
+// tree_attn_verify with its workspace passed separately: desc->workspace and
+// desc->workspace_bytes for the ABI call, the static scratch array for
+// tree_attn_verify_noalloc.
+int verify_with_workspace(const tree_attn_desc* d, void* workspace, size_t workspace_bytes,
+                          const void* q, const void* k_new, const void* v_new,
+                          const void* kv_pages, const int32_t* block_table,
+                          const int32_t* ctx_lens, const int32_t* tree_parent,
+                          const int32_t* tree_depth, void* out) {
   const int rc = check_common(d);
   if (rc != TA_OK) return rc;
   if (!q || !k_new || !v_new || !kv_pages || !block_table || !ctx_lens || !tree_parent ||
       !tree_depth || !out)
     return TA_ERR_NULL_POINTER;
   const Plan plan = make_plan(*d);
-  if (plan.bytes > 0 && (!d->workspace || d->workspace_bytes < plan.bytes))
-    return TA_ERR_WORKSPACE;
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes)) return TA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_pages) ||
       !aligned16(out) || !aligned16(d->rope_cos_sin) ||
-      (plan.bytes > 0 && !aligned16(d->workspace)))
+      (plan.bytes > 0 && !aligned16(workspace)))
     return TA_ERR_ALIGNMENT;
 
   VerifyParams p{};
@@ -125,7 +146,7 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
   p.n_cu = n_cu;
   if (plan.decode) return status_of(launch_verify_decode(p, stream));
   if (plan.mfma) {
-    char* ws = static_cast<char*>(d->workspace);
+    char* ws = static_cast<char*>(workspace);
     if (plan.splits > 1) {
       p.ws_ml = reinterpret_cast<float2*>(ws + plan.off_ml);
       p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
@@ -143,6 +164,55 @@ int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
     return status_of(e);
   }
   return status_of(launch_verify_simple(p, d->dtype, stream));
+}
+
+// Device address of `scratch` (defined at file scope above) on the current
+// device, set up on first use there: the address is taken with that device
+// current and kept per device, and the first 256 bytes (the persistent
+// kernel's work counters) are zeroed by a fill kernel on `stream`, ahead of
+// the caller's verify on the same stream.  nullptr if the device or the
+// symbol cannot be resolved or the fill cannot be enqueued.
+std::mutex scratch_mutex;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+void* scratch_on_current_device(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  ptr = scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  if (launch_fill_zero(ptr, 256, stream) != hipSuccess) return nullptr;
+  scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_attn_verify(const tree_attn_desc* d, const void* q, const void* k_new,
+                     const void* v_new, const void* kv_pages, const int32_t* block_table,
+                     const int32_t* ctx_lens, const int32_t* tree_parent,
+                     const int32_t* tree_depth, void* out) {
+  if (!d) return TA_ERR_NULL_POINTER;
+  return verify_with_workspace(d, d->workspace, d->workspace_bytes, q, k_new, v_new, kv_pages,
+                               block_table, ctx_lens, tree_parent, tree_depth, out);
+}
+
+int tree_attn_verify_noalloc(const tree_attn_desc* d, const void* q, const void* k_new,
+                             const void* v_new, const void* kv_pages,
+                             const int32_t* block_table, const int32_t* ctx_lens,
+                             const int32_t* tree_parent, const int32_t* tree_depth, void* out) {
+  const int rc = check_common(d);
+  if (rc != TA_OK) return rc;
+  if (make_plan(*d).bytes > kScratchBytes) return TA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device(static_cast<hipStream_t>(d->stream));
+  if (!ws) return TA_ERR_LAUNCH;
+  return verify_with_workspace(d, ws, kScratchBytes, q, k_new, v_new, kv_pages, block_table,
+                               ctx_lens, tree_parent, tree_depth, out);
 }
 
 int tree_accept_greedy(const tree_attn_desc* d, const int32_t* node_argmax,

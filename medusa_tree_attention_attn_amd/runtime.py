@@ -17,7 +17,8 @@ from ._lib import (TA_BF16, TA_F32, kv_commit_path, make_desc, tree_accept_commi
                    tree_accept_greedy, tree_accept_typical, tree_argmax_accept,
                    tree_medusa_candidates, tree_medusa_tree,
                    tree_vocab_argmax,
-                   tree_attn_rope_table, tree_attn_verify, tree_attn_workspace_init,
+                   tree_attn_rope_table, tree_attn_verify, tree_attn_verify_noalloc,
+                   tree_attn_workspace_init,
                    tree_attn_workspace_size)
 
 ROPE_BASE = 10000.0
@@ -60,6 +61,16 @@ class TreeVerifier:
             out = torch.empty_like(q)
         tree_attn_verify(self.desc, q, k_new, v_new, kv_pages, block_table, ctx_lens,
                          tree_parent, tree_depth, out)
+        return out
+
+    def verify_noalloc(self, q, k_new, v_new, kv_pages, block_table, ctx_lens, tree_parent,
+                       tree_depth, out):
+        """verify() through the allocation-free entry point: the library's
+        static device workspace instead of self.workspace, `out` given by the
+        caller."""
+        self._sync_stream()
+        tree_attn_verify_noalloc(self.desc, q, k_new, v_new, kv_pages, block_table, ctx_lens,
+                                 tree_parent, tree_depth, out)
         return out
 
     def accept(self, node_argmax, cand_tokens, tree_parent, accept_len=None, accept_path=None):

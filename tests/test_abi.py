@@ -371,3 +371,24 @@ def test_binding_raises_with_code(lib):
     with pytest.raises(ta.TreeAttnError) as e:
         ta.tree_attn_verify(desc, *[0x2000] * 9)
     assert e.value.code == -4
+
+
+def test_noalloc_rejects_a_plan_beyond_its_static_workspace(lib):
+    """The allocation-free verify keeps its split partials in a static 32 MiB
+    device array; a plan that needs more is refused on the host, before any
+    HIP call (no GPU is touched here)."""
+    d = _desc(batch=512, num_heads=32, num_kv_heads=32, max_ctx_len=65536,
+              max_blocks_per_seq=4096, num_blocks=1 << 20, rope_max_pos=65536 + 64,
+              split_tokens=512)
+    assert _lib.tree_attn_workspace_size(d) > 32 << 20
+    args = [0x2000 + 0x100 * i for i in range(9)]
+    assert lib.tree_attn_verify_noalloc(ctypes.byref(d), *args) == -8
+
+
+@pytest.mark.parametrize("kw, code", [(dict(t_max=65), -4), (dict(head_dim=96), -5),
+                                      (dict(block_size=8), -7)])
+def test_noalloc_descriptor_errors(lib, kw, code):
+    d = _desc(**kw)
+    args = [0x2000 + 0x100 * i for i in range(9)]
+    assert lib.tree_attn_verify_noalloc(ctypes.byref(d), *args) == code
+    assert lib.tree_attn_verify_noalloc(None, *args) == -1
