@@ -106,78 +106,46 @@ __device__ __forceinline__ void store_tile(const TileRegs& R, char* stage, int n
   }
 }
 
-// Q^T fragments of query row q for k-steps 0..7 (chunk 2*ks + g), rotated at
-// pos and pre-scaled by scale*log2 e.  Chunk c and chunk c+8 hold the RoPE
-// partners d and d+64, so the rotation stays inside the lane.  Loaded in two
-// steps so that the row and its (cos, sin) table row travel in different
-// round trips of the prologue.  These rows, and the tree rows below, keep the
-// default cache policy: the two wavefronts of a query tile read the same q
-// rows, and with the non-temporal hint on the q rows, the tree rows or both
-// the 7B-shaped batch-16 launch took 0.6-2.6 us longer.
-struct QRaw {
-  u32x4 x[8];   // x[s] = chunk 2s+g (d < 64), x[4+s] = chunk 2s+g+8
-};
-struct QRope {
-  f32x4 t[16];  // t[4s + j2] = (cos, sin) of k = 8(2s+g) + 2 j2 and k+1
-};
-__device__ __forceinline__ void load_q_raw(QRaw& Q, const uint16_t* qrow, int g) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    Q.x[s] = *reinterpret_cast<const u32x4*>(qrow + 8 * (2 * s + g));
-    Q.x[4 + s] = *reinterpret_cast<const u32x4*>(qrow + 64 + 8 * (2 * s + g));
-  }
-}
-__device__ __forceinline__ void load_q_rope(QRope& Rq, const float* cs, int g) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int j2 = 0; j2 < 4; ++j2)
-      Rq.t[4 * s + j2] = reinterpret_cast<const f32x4*>(cs + 2 * 8 * (2 * s + g))[j2];
-}
-__device__ __forceinline__ void rotate_q(u32x4 (&qf)[8], const QRaw& Q, const QRope& Rq,
-                                         float qscale) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    f32x8 y1, y2;
-#pragma unroll
-    for (int j2 = 0; j2 < 4; ++j2) {
-      const f32x4 t4 = Rq.t[4 * s + j2];
-      const float a0 = bf16_lo(Q.x[s][j2]), a1 = bf16_hi(Q.x[s][j2]);
-      const float b0 = bf16_lo(Q.x[4 + s][j2]), b1 = bf16_hi(Q.x[4 + s][j2]);
-      y1[2 * j2] = (a0 * t4[0] - b0 * t4[1]) * qscale;
-      y2[2 * j2] = (b0 * t4[0] + a0 * t4[1]) * qscale;
-      y1[2 * j2 + 1] = (a1 * t4[2] - b1 * t4[3]) * qscale;
-      y2[2 * j2 + 1] = (b1 * t4[2] + a1 * t4[3]) * qscale;
-    }
-    qf[s] = __builtin_bit_cast(u32x4, __builtin_convertvector(y1, bf16x8));
-    qf[s + 4] = __builtin_bit_cast(u32x4, __builtin_convertvector(y2, bf16x8));
-  }
-}
-
-// The tree block as a 64-token tile: key j = RoPE(k_new[b][j], ctx+depth[j])
-// with the commit's fixed-order fp32 arithmetic, rounded to bf16 as stored;
-// value j = v_new[b][j].  Nodes >= t_real are zero.  Thread tid rotates node
-// tid/4, dims 16*(tid%4) .. +15 and their partners; it copies V rows
-// 16*q4 + tid/16, chunk tid%16.
+// The tree block as a 64-token tile, and the queries.  Node j sits at
+// position ctx + depth[j], and one (cos, sin) table row serves both its key
+// and its query:
+//   * key j = RoPE(k_new[b][j]) with the commit's fixed-order fp32
+//     arithmetic, rounded to bf16 as the commit stores it; value j =
+//     v_new[b][j]; nodes >= t_real are zero;
+//   * query j = RoPE(q[b][j][h]) * scale * log2 e, rounded to bf16, written
+//     row-major to a query buffer from which every wavefront then reads its
+//     MFMA fragments (rows >= t_real are zero).
+// Thread tid rotates node tid/4, dims 16*(tid%4) .. +15 and their partners
+// (d + 64), of both rows; it copies V rows 16*q4 + tid/16, chunk tid%16.
+// Loading q this way needs the table row once per node instead of once per
+// query lane, which keeps the prologue's registers low enough to issue
+// context tiles 0 and 1 together.  These rows keep the default cache policy:
+// with the non-temporal hint on the q rows, the tree rows or both the
+// 7B-shaped batch-16 launch took 0.6-2.6 us longer.
 struct TreeRaw {
   u32x4 k[4];    // chunks 2u, 2u+1 (first half) and 8+2u, 9+2u (second half)
+  u32x4 q[4];    // the same chunks of the node's query row
   u32x4 v[4];
   f32x4 cs[8];   // (cos, sin) of k = 16u .. 16u+15
 };
-// Rows past last_row read row last_row instead (store_tree_tile zeroes every
-// row at or past t_real): the loads are unconditional, so the wavefront
-// issues all of them without waiting on any.
-__device__ __forceinline__ void load_tree_raw(TreeRaw& TR, const VerifyParams& p, int b, int hk,
-                                              int last_row, int tid) {
+// Tree rows past last_row (query rows past T - 1) read that row instead:
+// store_tree_tile zeroes every row at or past t_real, so the loads are
+// unconditional and the wavefront issues all of them without waiting on any.
+__device__ __forceinline__ void load_tree_raw(TreeRaw& TR, const VerifyParams& p, int b, int h,
+                                              int hk, int last_row, int tid) {
   const int T = p.T;
   const uint16_t* kn = static_cast<const uint16_t*>(p.k_new);
   const uint16_t* vn = static_cast<const uint16_t*>(p.v_new);
   const int j = min(tid >> 2, last_row), u = tid & 3;
   const uint16_t* row = kn + (((size_t)b * T + j) * p.Hkv + hk) * kD;
-  TR.k[0] = *reinterpret_cast<const u32x4*>(row + 16 * u);
-  TR.k[1] = *reinterpret_cast<const u32x4*>(row + 16 * u + 8);
-  TR.k[2] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u);
-  TR.k[3] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * u + 8);
+  const uint16_t* qrow =
+      static_cast<const uint16_t*>(p.q) + (((size_t)b * T + min(tid >> 2, T - 1)) * p.H + h) * kD;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int off = (i >> 1) * 64 + 16 * u + 8 * (i & 1);
+    TR.q[i] = *reinterpret_cast<const u32x4*>(qrow + off);
+    TR.k[i] = *reinterpret_cast<const u32x4*>(row + off);
+  }
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int jv = min(16 * q4 + (tid >> 4), last_row);
@@ -190,10 +158,12 @@ __device__ __forceinline__ void load_tree_rope(TreeRaw& TR, const float* rope, i
 #pragma unroll
   for (int i = 0; i < 8; ++i) TR.cs[i] = cs[i];
 }
-__device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, int t_real,
-                                                int tid) {
+constexpr int kQRow = 256 + 16;  // query buffer row (padded as the K rows)
+__device__ __forceinline__ void store_tree_tile(char* stage, char* qbuf, const TreeRaw& TR,
+                                                int t_real, float qscale, bool with_kv, int tid) {
   const int j = tid >> 2, u = tid & 3;
   u32x4 c[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  u32x4 e[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   if (j < t_real) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -207,9 +177,22 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
         // rounding does, for every finite value.
         c[h2][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y1a, y1b}, bf16x2));
         c[2 + h2][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y2a, y2b}, bf16x2));
+        float x1a, x2a, x1b, x2b;
+        rope_pair_exact(bf16_lo(TR.q[h2][w]), bf16_lo(TR.q[2 + h2][w]), t4[0], t4[1], x1a, x2a);
+        rope_pair_exact(bf16_hi(TR.q[h2][w]), bf16_hi(TR.q[2 + h2][w]), t4[2], t4[3], x1b, x2b);
+        e[h2][w] = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector(f32x2{x1a * qscale, x1b * qscale}, bf16x2));
+        e[2 + h2][w] = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector(f32x2{x2a * qscale, x2b * qscale}, bf16x2));
       }
     }
   }
+  char* qr = qbuf + j * kQRow;
+  *reinterpret_cast<u32x4*>(qr + 16 * (2 * u)) = e[0];
+  *reinterpret_cast<u32x4*>(qr + 16 * (2 * u + 1)) = e[1];
+  *reinterpret_cast<u32x4*>(qr + 16 * (8 + 2 * u)) = e[2];
+  *reinterpret_cast<u32x4*>(qr + 16 * (9 + 2 * u)) = e[3];
+  if (!with_kv) return;
   char* kr = stage + j * kKRow;
   *reinterpret_cast<u32x4*>(kr + 16 * (2 * u)) = c[0];
   *reinterpret_cast<u32x4*>(kr + 16 * (2 * u + 1)) = c[1];
@@ -221,6 +204,16 @@ __device__ __forceinline__ void store_tree_tile(char* stage, const TreeRaw& TR, 
     const int jv = 16 * q4 + (tid >> 4);
     *reinterpret_cast<u32x4*>(vb + 16 * q4 * kVRow) =
         jv < t_real ? TR.v[q4] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+// Q^T fragments of query row q for k-steps 0..7 from the query buffer: chunk
+// 2*ks + g for ks < 4, its RoPE partner chunk 8 + 2*(ks-4) + g for ks >= 4.
+__device__ __forceinline__ void load_q_frags(u32x4 (&qf)[8], const char* qbuf, int q, int g) {
+  const char* row = qbuf + q * kQRow;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int c = ks < 4 ? 2 * ks + g : 8 + 2 * (ks - 4) + g;
+    qf[ks] = *reinterpret_cast<const u32x4*>(row + 16 * c);
   }
 }
 
@@ -391,12 +384,9 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int row_l = min(lane, T - 1);
   const int par_raw = p.tree_parent[(size_t)b * T + row_l];
   const int dep_raw = p.tree_depth[(size_t)b * T + row_l];
-  QRaw Qr;  // rows q >= T are never used (row_real is false there)
-  load_q_raw(Qr,
-             static_cast<const uint16_t*>(p.q) + (((size_t)b * T + min(q, T - 1)) * p.H + h) * kD,
-             g);
-  TreeRaw TR;  // only split 0 uses it: the others read row 0 over and over
-  load_tree_raw(TR, p, b, hk, sp == 0 ? T - 1 : 0, tid);
+  TreeRaw TR;  // every split rotates its queries; only split 0 uses the tree k/v rows (the
+               // others read row 0 over and over)
+  load_tree_raw(TR, p, b, h, hk, sp == 0 ? T - 1 : 0, tid);
 
   const int ctx = clampi(ctx_raw, 0, p.max_ctx);
   const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
@@ -430,30 +420,18 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const bool active = qt < nqt;
   const uint64_t anc_q = __shfl(anc, q);
   const bool row_real = active && q < t_real;
-  const int pos_q = ctx + clampi(__shfl(dep, q), 0, T - 1);
   const int pos_j = ctx + clampi(__shfl(dep, tid >> 2), 0, T - 1);
 
   lds_sync();  // s_pages visible; the q and tree k/v rows may still be in flight
-  // ---- round trip 2: the (cos, sin) rows and context tile 0; tile 1 follows
-  // once q is rotated, and the tree tile is built and computed while it
-  // loads.
+  // ---- round trip 2: the (cos, sin) rows and context tiles 0 and 1; the
+  // queries are rotated and the tree tile is built and computed while the
+  // tiles load.
   Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv, max(npages - 1, 0)};
   const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
-  QRope Rq;
-  load_q_rope(Rq, p.rope + (size_t)pos_q * kD, g);
-  load_tree_rope(TR, p.rope, pos_j, tid);  // split 0 uses it; a valid row for every split
+  load_tree_rope(TR, p.rope, pos_j, tid);  // node tid/4's row: its key and its query
   TileRegs R0;  // context tile 0
   TileRegs R;   // context tile t + 1 while tile t is computed
   load_ctx_tile(R0, G, c0, tid);  // unconditional: the compiler counts the loads
-
-  u32x4 qf[8];
-  if (row_real) {
-    rotate_q(qf, Qr, Rq, p.scale * kLog2e);
-  } else {
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) qf[s2] = u32x4{0u, 0u, 0u, 0u};
-  }
-  // Issued once the q row and its table row are no longer held.
   load_ctx_tile(R, G, c0 + kTile, tid);
 
   WaveState st;
@@ -463,15 +441,24 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   char* stage1 = smem + kStageBytes;
 
   const LaneOffs L = lane_offsets(lane, th, kKBytes);
-  // The tree tile goes through stage 1 while context tiles 0 and 1 load.
-  if (sp == 0) {
-    store_tree_tile(stage1, TR, t_real, tid);
-    lds_sync();
+  // While context tiles 0 and 1 load, the rotated queries go to a stage that
+  // is free until a tile is stored there: split 0 puts its tree tile in
+  // stage 1 and its queries in stage 0 (one more barrier before tile 0 takes
+  // stage 0); the other splits put their queries in stage 1, which tile 1
+  // only takes after the barrier that follows tile 0's store.
+  static_assert(kTile * kQRow <= kStageBytes, "query buffer in a stage");
+  char* qbuf = sp == 0 ? stage0 : stage1;
+  store_tree_tile(stage1, qbuf, TR, t_real, p.scale * kLog2e, sp == 0, tid);
+  lds_sync();
+  u32x4 qf[8];
+  load_q_frags(qf, qbuf, q, g);
+  if (sp == 0) {  // uniform
     if (active) compute_tile<kTreeTile>(st, qf, stage1, L, kTile, anc_q);
+    lds_sync();  // query buffer read by every wavefront: stage 0 takes tile 0
   }
   auto rows_of = [&](int t) { return min(kTile, c1 - (c0 + kTile * t)); };
   if (n_tiles > 0) store_tile(R0, stage0, rows_of(0), tid);
-  lds_sync();  // stage 0 filled, stage 1's tree reads done; tile 1 stays in flight
+  lds_sync();  // stage 0 filled; stage 1's tree or query reads done; tile 1 stays in flight
   if (n_tiles > 0) {
     // Every tile but the last is full: one straight-line path, no masking.
     for (int t = 0; t < n_tiles - 1; ++t) {
