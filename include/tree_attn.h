@@ -82,9 +82,7 @@ enum ta_flags {
   TA_FLAG_PERSISTENT_KERNEL = 4 /* MFMA verify: one resident workgroup per CU   */
                               /* taking work items from a counter.  Without    */
                               /* either flag the library takes the decode      */
-                              /* kernel when t_max == 1, else the persistent   */
-                              /* kernel when there are at least 4 work items   */
-                              /* per CU, else the grid kernel.                 */
+                              /* kernel when t_max == 1, else the grid kernel. */
 };
 
 enum ta_status {

@@ -77,8 +77,7 @@ int tree_attn_plan_info(const tree_attn_desc* d, int32_t* kernel, int32_t* split
   if (plan.decode) {
     k = TA_KERNEL_DECODE;
   } else if (plan.mfma) {
-    const long long items = (long long)d->batch * d->num_heads * plan.splits;
-    k = use_stream_kernel(*d, items, device_cu_count()) ? TA_KERNEL_PERSISTENT : TA_KERNEL_GRID;
+    k = use_stream_kernel(*d) ? TA_KERNEL_PERSISTENT : TA_KERNEL_GRID;
   }
   if (kernel) *kernel = k;
   if (splits) *splits = plan.splits;
@@ -152,8 +151,7 @@ int verify_with_workspace(const tree_attn_desc* d, void* workspace, size_t works
       p.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
     }
     hipError_t e;
-    const long long items = (long long)p.B * p.H * p.splits;
-    if (use_stream_kernel(*d, items, n_cu)) {
+    if (use_stream_kernel(*d)) {
       if (n_cu <= 0) return TA_ERR_LAUNCH;
       p.ws_ctr = reinterpret_cast<uint32_t*>(ws + plan.off_ctr);
       e = launch_verify_stream(p, stream);

@@ -264,8 +264,8 @@ def test_medusa_candidates_checks_the_table(lib):
 
 def test_plan_info_follows_flags(lib):
     """The kernel choice is a host-side rule: forced by the flags, else the
-    persistent kernel only with >= 4 work items per CU (no device here: 0 CUs,
-    so the grid kernel); splits come from the context bound."""
+    grid kernel (the persistent kernel only when forced); splits come from
+    the context bound."""
     out = [ctypes.c_int32() for _ in range(3)]
     refs = [ctypes.byref(x) for x in out]
     assert lib.tree_attn_plan_info(ctypes.byref(_desc()), *refs) == 0
