@@ -566,7 +566,7 @@ def main():
     ap.add_argument("--workload", default="vicuna7b_b16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--kernel", choices=("auto", "grid", "persistent", "simple"),
+    ap.add_argument("--kernel", choices=("auto", "grid", "persistent", "simple", "decode"),
                     default="auto", help="verify kernel (auto: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-posterior", action="store_true",
@@ -626,7 +626,8 @@ def main():
                       head_dim=s.head_dim, max_blocks_per_seq=wl.max_blocks,
                       num_blocks=wl.num_blocks, max_ctx_len=wl.max_ctx_len,
                       dtype=wl.torch_dtype, split_tokens=args.split_tokens,
-                      flags={"auto": 0, "simple": 1, "grid": 2, "persistent": 4}[args.kernel])
+                      flags={"auto": 0, "simple": 1, "grid": 2, "persistent": 4,
+                             "decode": 8}[args.kernel])
     from medusa_tree_attention_attn_amd._lib import tree_attn_plan_info
     kernel_name, n_splits, split_tokens = tree_attn_plan_info(tv.desc)
     log(f"{copies} rotating input copies ({copies * pool_bytes / 1e9:.2f} GB of KV pool), "

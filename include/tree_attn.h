@@ -79,10 +79,16 @@ enum ta_flags {
   TA_FLAG_SIMPLE_KERNEL = 1,  /* verify with the plain one-wavefront-per-node  */
                               /* kernel even where the MFMA kernels apply      */
   TA_FLAG_GRID_KERNEL = 2,    /* MFMA verify: one workgroup per work item      */
-  TA_FLAG_PERSISTENT_KERNEL = 4 /* MFMA verify: one resident workgroup per CU   */
-                              /* taking work items from a counter.  Without    */
-                              /* either flag the library takes the decode      */
-                              /* kernel when t_max == 1, else the grid kernel. */
+  TA_FLAG_PERSISTENT_KERNEL = 4, /* MFMA verify: one resident workgroup per CU  */
+                              /* taking work items from a counter.             */
+  TA_FLAG_DECODE_KERNEL = 8   /* t_max == 1 (bf16, head_dim 128): the decode   */
+                              /* kernel, one workgroup per (sequence, head).   */
+                              /* Without a flag the library takes the decode   */
+                              /* kernel when t_max == 1 and max_ctx_len <=     */
+                              /* 1024, else the grid kernel, which sends work  */
+                              /* items whose tree has at most 2 real nodes     */
+                              /* (sequences of at most 64 work-item groups) to */
+                              /* its vector-ALU small-tree path.               */
 };
 
 enum ta_status {
@@ -314,9 +320,10 @@ size_t tree_attn_workspace_size(const tree_attn_desc* desc);
 
 /* Kernels tree_attn_verify launches for this descriptor on the current
  * device: *kernel = TA_KERNEL_SIMPLE, TA_KERNEL_GRID, TA_KERNEL_PERSISTENT or
- * TA_KERNEL_DECODE (t_max == 1 with bf16 and head_dim 128 and neither MFMA
- * flag: one workgroup per (sequence, head) streams its whole context, no
- * splits, no workspace); *splits = context splits per (sequence, head) (a
+ * TA_KERNEL_DECODE (t_max == 1 with bf16 and head_dim 128, and either
+ * TA_FLAG_DECODE_KERNEL or max_ctx_len <= 1024 without an MFMA flag: one
+ * workgroup per (sequence, head) streams its whole context, no splits, no
+ * workspace); *splits = context splits per (sequence, head) (a
  * merge kernel follows when it is > 1); *split_tokens = context tokens per
  * split.  Output pointers may be NULL.  Host-only query; errors as
  * tree_attn_verify's descriptor checks. */

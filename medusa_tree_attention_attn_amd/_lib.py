@@ -26,6 +26,7 @@ TA_F32 = 1
 TA_FLAG_SIMPLE_KERNEL = 1
 TA_FLAG_GRID_KERNEL = 2
 TA_FLAG_PERSISTENT_KERNEL = 4
+TA_FLAG_DECODE_KERNEL = 8
 
 STATUS = {
     0: "TA_OK", -1: "TA_ERR_NULL_POINTER", -2: "TA_ERR_BAD_DIMS", -3: "TA_ERR_DTYPE",

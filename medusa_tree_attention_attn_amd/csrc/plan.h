@@ -50,11 +50,19 @@ inline bool use_stream_kernel(const tree_attn_desc& d) {
   return (d.flags & TA_FLAG_PERSISTENT_KERNEL) && !(d.flags & TA_FLAG_GRID_KERNEL);
 }
 
+// One-node trees (t_max == 1): the decode kernel below this context bound,
+// the grid kernel (whose small-tree path streams the context on the vector
+// ALU) above it.  Measured, batch 64: contexts 128..512 decode kernel 73.5
+// against 77.9 us; 128..8192 624 against 637 us for the grid kernel; batch
+// 256, contexts 128..2048: 706 against 746 us.
+constexpr int kDecodeMaxCtx = 1024;
+
 inline Plan make_plan(const tree_attn_desc& d) {
   Plan p{};
   p.mfma = d.dtype == TA_BF16 && d.head_dim == 128 && !(d.flags & TA_FLAG_SIMPLE_KERNEL);
+  const bool forced = d.flags & (TA_FLAG_GRID_KERNEL | TA_FLAG_PERSISTENT_KERNEL);
   p.decode = p.mfma && d.t_max == 1 &&
-             !(d.flags & (TA_FLAG_GRID_KERNEL | TA_FLAG_PERSISTENT_KERNEL));
+             ((d.flags & TA_FLAG_DECODE_KERNEL) || (!forced && d.max_ctx_len <= kDecodeMaxCtx));
   p.stream = p.mfma && !p.decode;
   const int max_ctx = d.max_ctx_len > 0 ? d.max_ctx_len : 1;
   if (p.decode) {  // one workgroup streams a whole context; nothing to merge

@@ -23,7 +23,7 @@
 // the commit's fixed-order arithmetic and rounded to bf16, as the commit
 // will store it) joins wavefront 0's group 0 after the context.
 #include "launch.h"
-#include "mfma_tile.h"
+#include "page_stream.h"
 
 namespace ta {
 namespace {
@@ -40,37 +40,9 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDepth = TA_DECODE_DEPTH;
 constexpr int kWinPages = 2048;  // block ids staged in LDS at a time
 
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
-// (The words are copied out first: hipcc lowers a bit cast taken straight
-// from a vector element to element 0 for every index.)
-__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t aw = a[w], bw = b[w];
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, aw),
-                                          __builtin_bit_cast(bf16x2v, bw), acc, false);
-  }
-  return acc;
-}
-
-// Sum over the 16 lanes of a lane group.
-__device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
-}
-
 struct Page {
   u32x4 k[4];
   u32x4 v[4];
-};
-
-struct State {
-  float m, l;
-  float o[8];
 };
 
 // The pages are read once: the loads carry the non-temporal hint (batch 64,
@@ -83,31 +55,6 @@ __device__ __forceinline__ void load_page(Page& P, const uint16_t* kbase, size_t
     P.v[i] = __builtin_nontemporal_load(
         reinterpret_cast<const u32x4*>(kbase + v_plane + 512 * i + 8 * lane));
   }
-}
-
-// Adds up to four tokens (scores s[i], values v[i]) to the group's state;
-// tokens with s = -inf add nothing.
-__device__ __forceinline__ void add_tokens(State& st, const float (&s)[4], const u32x4 (&v)[4]) {
-  const float mp = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  const float mn = fmaxf(st.m, mp);
-  if (mn == -INFINITY) return;  // nothing valid yet
-  const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // st.m = -inf -> 0
-  float p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - mn);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    float a0 = st.o[2 * w] * alpha, a1 = st.o[2 * w + 1] * alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a0 = fmaf(p[i], bf16_lo(v[i][w]), a0);
-      a1 = fmaf(p[i], bf16_hi(v[i][w]), a1);
-    }
-    st.o[2 * w] = a0;
-    st.o[2 * w + 1] = a1;
-  }
-  st.m = mn;
 }
 
 // (b, h) of launch slot `slot`: with at most 64 sequences, sequences are
@@ -174,10 +121,7 @@ __global__ __launch_bounds__(kDecThreads) void verify_decode_kernel(VerifyParams
   }
 
   State st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.o[i] = 0.f;
+  reset(st);
 
   // The context in windows of kWinPages pages whose block ids (checked)
   // are first copied to LDS, so that no page address waits on a vector

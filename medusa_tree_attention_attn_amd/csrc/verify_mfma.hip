@@ -35,6 +35,7 @@
 // tiles; the tree tile is built and computed while those tiles load.
 #include "launch.h"
 #include "mfma_tile.h"
+#include "page_stream.h"
 #include "plan.h"
 
 namespace ta {
@@ -304,6 +305,255 @@ __device__ __forceinline__ void write_partial_half(const WaveState& st, const Ve
   if (write_ml && g == 0) p.ws_ml[row] = float2{st.m, st.l};
 }
 
+// ---------------------------------------------------------------------------
+// Small trees (at most kSmallTree = 2 real nodes, e.g. the one-node rows of
+// a mixed batch where speculation is off for some sequences): a 32-query
+// matrix-core tile would be mostly padding, so the item keeps the page
+// streamer and the prologue of the tree path (page ids in LDS, rotated
+// queries and the tree tile in LDS, context tiles 0 and 1 in flight in
+// registers) and then consumes each context tile straight from its
+// registers on the vector ALU, as the one-node decode kernel does: thread
+// tid holds dims 8 (tid % 16) .. +7 of K and V of token 16 p + tid / 16 of
+// the tile (p = 0..3), so lane group tid / 16 of the workgroup scores its
+// four tokens against every query with dot2 sums over 16 lanes and keeps
+// one online-softmax state per query.  No tile goes through LDS and no
+// barrier sits in the loop; each tile's registers take the tile two ahead
+// once consumed.  The tree keys join lane groups 0..7 (node 4 w + g of
+// wavefront w, group g), masked by each query's ancestor bitmask.  The 16
+// states of each query are merged through LDS at the end.  The item is
+// routed here at launch (the tree row at index kSmallTree is padding), so
+// the two paths share no registers (the kernel keeps its 243 VGPRs; 8
+// queries, 80 VGPRs of states beside two register tiles, spilled).  The
+// vector-ALU work grows with the queries while the matrix-core tile does
+// not, so the cut is at 2 nodes.  Measured on stress-shaped batches of 64
+// sequences (contexts 128..8192) whose trees all have 1, 2 or 4 nodes: 672,
+// 679 and 691 us on this path against 682, 686 and 686 us on the matrix
+// cores; one-node trees at batch 64 624 us against 637 us for the decode
+// kernel.
+// ---------------------------------------------------------------------------
+constexpr int kSmallTree = 2;
+
+template <int kM>
+__device__ __forceinline__ void small_tree_item(const VerifyParams& p, const Geo& G, TreeRaw& TR,
+                                                int pos_j, char* smem, int n_tiles, int c0,
+                                                int c1, int b, int h, int sp, int nsplit,
+                                                int t_real, uint64_t anc, int tid) {
+  const int lane = tid & 63, wv = tid >> 6, grp = lane >> 4, dc = lane & 15;
+  const int T = p.T;
+  // Round trip 2 as on the matrix-core path: the (cos, sin) rows and context
+  // tiles 0 and 1; the rotated queries go to stage 0, the tree tile to
+  // stage 1 (no context tile goes through LDS here).
+  load_tree_rope(TR, p.rope, pos_j, tid);
+  TileRegs R0, R;
+  load_ctx_tile(R0, G, c0, tid);
+  load_ctx_tile(R, G, c0 + kTile, tid);
+  const char* qbuf = smem;
+  const char* tree_stage = smem + kStageBytes;
+  store_tree_tile(smem + kStageBytes, smem, TR, t_real, p.scale * kLog2e, sp == 0, tid);
+  lds_sync();
+  u32x4 qv[kM];       // the lane's 8 dims of each query (rows >= t_real are zero)
+  uint32_t anc_m[kM];  // ancestor-or-self bitmask of each query (nodes < 8: low word), uniform
+  State st[kM];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    qv[m] = *reinterpret_cast<const u32x4*>(qbuf + m * kQRow + 16 * dc);
+    anc_m[m] = __builtin_amdgcn_readfirstlane((uint32_t)__shfl(anc, m));
+    reset(st[m]);
+  }
+  // This lane group's tokens of tile t: c0 + 64 t + 16 pp + tid / 16.  Rows
+  // past the split's end (the last page's tail, or a page re-read past the
+  // end) are masked, and their values zeroed.
+  const int tok_lane = c0 + (tid >> 4);
+  auto consume = [&](const TileRegs& X, int t) {
+    const int tok = tok_lane + kTile * t;
+    u32x4 v[4];
+    bool ok[4];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      ok[pp] = tok + 16 * pp < c1;
+      v[pp] = ok[pp] ? X.v[pp] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      float s[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float d = group_sum(dot8(qv[m], X.k[pp], 0.f));
+        s[pp] = ok[pp] ? d : -INFINITY;
+      }
+      add_tokens(st[m], s, v);
+    }
+  };
+  // Tile 0 (R0) is consumed first; then the tiles alternate between R and a
+  // second register tile, each refilled with the tile two ahead.
+  TileRegs R2;
+  if (n_tiles > 0) {
+    load_ctx_tile(R2, G, c0 + 2 * kTile, tid);
+    consume(R0, 0);
+  }
+  int t = 1;
+#pragma unroll 1
+  for (; t + 1 < n_tiles; t += 2) {
+    consume(R, t);
+    load_ctx_tile(R, G, c0 + kTile * (t + 2), tid);
+    consume(R2, t + 1);
+    load_ctx_tile(R2, G, c0 + kTile * (t + 3), tid);
+  }
+  if (t < n_tiles) consume(R, t);
+  if (sp == 0 && wv < 2) {  // the tree keys, rotated as stored (zero rows past t_real)
+    const int j = 4 * wv + grp;
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(tree_stage + j * kKRow + 16 * dc);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(tree_stage + kKBytes + j * kVRow + 16 * dc);
+    const u32x4 v4[4] = {vv, vv, vv, vv};
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const float d = group_sum(dot8(qv[m], kk, 0.f));
+      const float s4[4] = {(j < t_real && ((anc_m[m] >> j) & 1u)) ? d : -INFINITY, -INFINITY,
+                           -INFINITY, -INFINITY};
+      add_tokens(st[m], s4, v4);
+    }
+  }
+  // Merge the 16 lane-group states of each query through LDS.
+  __syncthreads();  // the query buffer and the tree tile are no longer read
+  float* s_o = reinterpret_cast<float*>(smem);  // [16 states][kM][128]
+  float* s_ml = s_o + 16 * kM * kD;             // [16 states][kM][2]
+  const int si = tid >> 4;
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    float* o = s_o + (si * kM + m) * kD + 8 * dc;
+    *reinterpret_cast<f32x4*>(o) = f32x4{st[m].o[0], st[m].o[1], st[m].o[2], st[m].o[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{st[m].o[4], st[m].o[5], st[m].o[6], st[m].o[7]};
+    if (dc == 0) {
+      s_ml[(si * kM + m) * 2] = st[m].m;
+      s_ml[(si * kM + m) * 2 + 1] = st[m].l;
+    }
+  }
+  __syncthreads();
+  const int bh = b * p.H + h;
+  for (int idx = tid; idx < kM * (kD / 4); idx += kThreads) {
+    const int m = idx / (kD / 4), d4 = 4 * (idx % (kD / 4));
+    if (m >= t_real) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) M = fmaxf(M, s_ml[(s2 * kM + m) * 2]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const float w = __builtin_amdgcn_exp2f(s_ml[(s2 * kM + m) * 2] - Mu);  // -inf -> 0
+      L += w * s_ml[(s2 * kM + m) * 2 + 1];
+      o += w * *reinterpret_cast<const f32x4*>(s_o + (s2 * kM + m) * kD + d4);
+    }
+    if (nsplit == 1) {
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + (((size_t)b * T + m) * p.H + h) * kD +
+                                d4) = __builtin_bit_cast(u32x2, __builtin_convertvector(o * inv, bf16x4));
+    } else {
+      const size_t row = ((size_t)bh * p.splits + sp) * T + m;
+      *reinterpret_cast<f32x4*>(p.ws_o + row * kD + d4) = o;
+      if (d4 == 0) p.ws_ml[row] = float2{M, L};
+    }
+  }
+  if (nsplit == 1) {  // padding rows (and rows past the real ones) are zeros
+    for (int idx = tid; idx < (T - t_real) * 16; idx += kThreads) {
+      const int m = t_real + (idx >> 4), ch = idx & 15;
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + (((size_t)b * T + m) * p.H + h) * kD +
+                                8 * ch) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// What round trip 1 of a work item leaves: its context bounds, and the
+// tree structure with one lane per node (every wavefront computes it).
+struct ItemMeta {
+  int ctx, nsplit, c1, npages;
+  int t_real;     // real nodes (a prefix of the rows)
+  uint64_t anc;   // ancestor-or-self bitmask of node `lane`
+  int dep;        // depth of node `lane`
+  int pos_j;      // position of node tid/4: ctx + its depth
+};
+
+// ---- Round trip 1: ctx_len, page ids, tree rows, then the q rows and the
+// tree k/v rows.  Every load is unconditional (row indices clamped into
+// their arrays, values masked where they are used), so the wavefront issues
+// them back to back; the page ids go to s_pages (visible after the caller's
+// next LDS barrier, which waits for them and the tree rows alone: the q and
+// tree k/v rows stay in flight into round trip 2).  Returns false (uniform)
+// when the split lies beyond the context.
+__device__ __forceinline__ bool item_round_trip1(const VerifyParams& p, int b, int h, int hk,
+                                                 int sp, int c0, int* s_pages, TreeRaw& TR,
+                                                 ItemMeta& M, int tid) {
+  const int lane = tid & 63;
+  const int T = p.T;
+  const int ctx_raw = p.ctx_lens[b];
+  // c0 < max(max_ctx, 1) <= 16 * max_blocks for every split of the plan, so
+  // max_pages >= 1 and the clamped page index stays inside the table row.
+  const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks + (c0 >> 4);
+  const int max_pages = min(p.chunk / kPage, p.max_blocks - (c0 >> 4));
+  static_assert(kMaxSplitPages <= 2 * kThreads, "two page ids per thread");
+  const int blk_raw0 = table_row[min(tid, max_pages - 1)];
+  const int blk_raw1 = table_row[min(tid + kThreads, max_pages - 1)];
+  const int row_l = min(lane, T - 1);
+  const int par_raw = p.tree_parent[(size_t)b * T + row_l];
+  const int dep_raw = p.tree_depth[(size_t)b * T + row_l];
+  // Every split rotates its queries; only split 0 uses the tree k/v rows (the
+  // others read row 0 over and over).
+  load_tree_raw(TR, p, b, h, hk, sp == 0 ? T - 1 : 0, tid);
+
+  M.ctx = clampi(ctx_raw, 0, p.max_ctx);
+  M.nsplit = M.ctx == 0 ? 1 : (M.ctx + p.chunk - 1) / p.chunk;
+  if (sp >= M.nsplit) return false;
+  M.c1 = min(M.ctx, c0 + p.chunk);
+  M.npages = (M.c1 - c0 + kPage - 1) / kPage;  // <= max_pages
+  // Entry 0 is written even for an empty split: the first two tiles load
+  // unconditionally.
+  if (tid < max(M.npages, 1))
+    s_pages[tid] = (tid < M.npages && blk_raw0 >= 0 && blk_raw0 < p.num_blocks) ? blk_raw0 : 0;
+  if (tid + kThreads < M.npages)
+    s_pages[tid + kThreads] = (blk_raw1 >= 0 && blk_raw1 < p.num_blocks) ? blk_raw1 : 0;
+  const int par = lane < T ? par_raw : kPadParent;
+  M.dep = lane < T ? dep_raw : 0;
+
+  const bool real = lane < T && par != kPadParent;
+  const uint64_t real_mask = __ballot(real);
+  M.t_real = real_mask == ~0ull ? 64 : __builtin_ctzll(~real_mask);  // real prefix
+  const bool linked = lane < M.t_real && (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+  uint64_t anc = linked ? (1ull << lane) : 0ull;
+  int up = (linked && lane > 0) ? par : lane;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const uint64_t a_up = __shfl(anc, up);
+    const int up_up = __shfl(up, up);
+    anc |= a_up;
+    up = up_up;
+  }
+  M.anc = anc;
+  M.pos_j = M.ctx + clampi(__shfl(M.dep, tid >> 2), 0, T - 1);
+  return true;
+}
+
+// A work item whose tree has at most kSmallTree real nodes: round trip 1 as
+// on the matrix-core path, then the vector-ALU path above.
+__device__ __forceinline__ void small_tree_workgroup(const VerifyParams& p, int b, int h, int sp,
+                                                     char* smem, int* s_pages, int tid) {
+  const int hk = h / (p.H / p.Hkv);
+  const int c0 = sp * p.chunk;
+  TreeRaw TR;
+  ItemMeta M;
+  if (!item_round_trip1(p, b, h, hk, sp, c0, s_pages, TR, M, tid)) return;  // uniform
+  lds_sync();  // s_pages visible
+  const Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv,
+              max(M.npages - 1, 0)};
+  const int n_tiles = (M.c1 - c0 + kTile - 1) / kTile;
+  if (M.t_real <= 1)
+    small_tree_item<1>(p, G, TR, M.pos_j, smem, n_tiles, c0, M.c1, b, h, sp, M.nsplit, M.t_real,
+                       M.anc, tid);
+  else
+    small_tree_item<2>(p, G, TR, M.pos_j, smem, n_tiles, c0, M.c1, b, h, sp, M.nsplit, M.t_real,
+                       M.anc, tid);
+}
+
 // Launch slot -> (sequence, head, split).  A (sequence, split) group holds H
 // work items of the same length (the split's tokens).  With at most 64
 // groups, the groups that exist are ranked by length (longest first, equal
@@ -317,8 +567,9 @@ __device__ __forceinline__ void write_partial_half(const WaveState& st, const Ve
 // frees up first.  With more than 64 groups the order is (sequence, head)
 // major, split minor.  Every lane of the wavefront takes part (lane = group).
 __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int lane, int& b,
-                                            int& h, int& sp) {
+                                            int& h, int& sp, bool& small) {
   const int G = p.B * p.splits;
+  small = false;
   if (G > 64 || p.n_cu <= 0) {
     b = (slot / p.splits) / p.H;
     h = (slot / p.splits) % p.H;
@@ -326,11 +577,17 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
     return true;
   }
   int len = -1;  // tokens of the group's split; -1: the split does not exist
+  int small_l = 0;  // the group's tree has at most kSmallTree real nodes
   if (lane < G) {
     const int j = lane / p.splits, s = lane - j * p.splits;
-    const int c = clampi(p.ctx_lens[j], 0, p.max_ctx);
+    const int ctx_raw = p.ctx_lens[j];
+    const int par_cut = p.tree_parent[(size_t)j * p.T + min(kSmallTree, p.T - 1)];
+    const int c = clampi(ctx_raw, 0, p.max_ctx);
     const int n = c == 0 ? 1 : (c + p.chunk - 1) / p.chunk;
     if (s < n) len = min(p.chunk, c - s * p.chunk);
+    // Real nodes form a prefix, so a padding node at index kSmallTree (or a
+    // tree of at most kSmallTree rows) bounds the real ones by kSmallTree.
+    small_l = p.T <= kSmallTree || par_cut == kPadParent;
   }
   const int N = __popcll(__ballot(len >= 0)) * p.H;
   if (slot >= N) return false;  // uniform
@@ -347,6 +604,7 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
   const int grp = hit ? __builtin_ctzll(hit) : 0;
   b = grp / p.splits;
   sp = grp - b * p.splits;
+  small = __shfl(small_l, grp) != 0;
   return true;
 }
 
@@ -360,67 +618,28 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int qt = wv >> 1, th = wv & 1;
   const int g = lane >> 5, r32 = lane & 31;
   int b, h, sp;
-  if (!launch_item(p, blockIdx.x, lane, b, h, sp)) return;
+  bool small;
+  if (!launch_item(p, blockIdx.x, lane, b, h, sp, small)) return;
+  if (small) {  // uniform: a tree of at most kSmallTree real nodes
+    small_tree_workgroup(p, b, h, sp, smem, s_pages, tid);
+    return;
+  }
   const int bh = b * p.H + h;
   const int hk = h / (p.H / p.Hkv);
   const int T = p.T;
   const int q = 32 * qt + r32;
   const int c0 = sp * p.chunk;
 
-  // ---- round trip 1: ctx_len, page ids, tree rows, then the q row and the
-  // tree k/v rows.  Every load is unconditional (row indices clamped into
-  // their arrays, values masked where they are used), so the wavefront issues
-  // them back to back; the LDS-only barrier below waits for the page ids and
-  // tree rows alone, and the q and tree k/v rows stay in flight into round
-  // trip 2.
-  const int ctx_raw = p.ctx_lens[b];
-  // c0 < max(max_ctx, 1) <= 16 * max_blocks for every split of the plan, so
-  // max_pages >= 1 and the clamped page index stays inside the table row.
-  const int32_t* table_row = p.block_table + (size_t)b * p.max_blocks + (c0 >> 4);
-  const int max_pages = min(p.chunk / kPage, p.max_blocks - (c0 >> 4));
-  static_assert(kMaxSplitPages <= 2 * kThreads, "two page ids per thread");
-  const int blk_raw0 = table_row[min(tid, max_pages - 1)];
-  const int blk_raw1 = table_row[min(tid + kThreads, max_pages - 1)];
-  const int row_l = min(lane, T - 1);
-  const int par_raw = p.tree_parent[(size_t)b * T + row_l];
-  const int dep_raw = p.tree_depth[(size_t)b * T + row_l];
-  TreeRaw TR;  // every split rotates its queries; only split 0 uses the tree k/v rows (the
-               // others read row 0 over and over)
-  load_tree_raw(TR, p, b, h, hk, sp == 0 ? T - 1 : 0, tid);
-
-  const int ctx = clampi(ctx_raw, 0, p.max_ctx);
-  const int nsplit = ctx == 0 ? 1 : (ctx + p.chunk - 1) / p.chunk;
-  if (sp >= nsplit) return;  // uniform: the whole workgroup leaves
-  const int c1 = min(ctx, c0 + p.chunk);
-  const int npages = (c1 - c0 + kPage - 1) / kPage;  // <= max_pages
-  // Entry 0 is written even for an empty split: the first two tiles load
-  // unconditionally.
-  if (tid < max(npages, 1))
-    s_pages[tid] = (tid < npages && blk_raw0 >= 0 && blk_raw0 < p.num_blocks) ? blk_raw0 : 0;
-  if (tid + kThreads < npages)
-    s_pages[tid + kThreads] = (blk_raw1 >= 0 && blk_raw1 < p.num_blocks) ? blk_raw1 : 0;
-  const int par = lane < T ? par_raw : kPadParent;
-  const int dep = lane < T ? dep_raw : 0;
-
-  // Tree structure, one lane per node (every wavefront computes it).
-  const bool real = lane < T && par != kPadParent;
-  const uint64_t real_mask = __ballot(real);
-  const int t_real = real_mask == ~0ull ? 64 : __builtin_ctzll(~real_mask);  // real prefix
-  const bool linked = lane < t_real && (lane == 0 ? par == -1 : (par >= 0 && par < lane));
-  uint64_t anc = linked ? (1ull << lane) : 0ull;
-  int up = (linked && lane > 0) ? par : lane;
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    const uint64_t a_up = __shfl(anc, up);
-    const int up_up = __shfl(up, up);
-    anc |= a_up;
-    up = up_up;
-  }
+  TreeRaw TR;
+  ItemMeta M;
+  if (!item_round_trip1(p, b, h, hk, sp, c0, s_pages, TR, M, tid)) return;  // uniform
+  const int ctx = M.ctx, nsplit = M.nsplit, c1 = M.c1, npages = M.npages, t_real = M.t_real;
+  const uint64_t anc = M.anc;
+  const int pos_j = M.pos_j;
   const int nqt = t_real > 32 ? 2 : 1;
   const bool active = qt < nqt;
   const uint64_t anc_q = __shfl(anc, q);
   const bool row_real = active && q < t_real;
-  const int pos_j = ctx + clampi(__shfl(dep, tid >> 2), 0, T - 1);
 
   lds_sync();  // s_pages visible; the q and tree k/v rows may still be in flight
   // ---- round trip 2: the (cos, sin) rows and context tiles 0 and 1; the
@@ -434,13 +653,8 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   load_ctx_tile(R0, G, c0, tid);  // unconditional: the compiler counts the loads
   load_ctx_tile(R, G, c0 + kTile, tid);
 
-  WaveState st;
-  reset(st);
-
   char* stage0 = smem;
   char* stage1 = smem + kStageBytes;
-
-  const LaneOffs L = lane_offsets(lane, th, kKBytes);
   // While context tiles 0 and 1 load, the rotated queries go to a stage that
   // is free until a tile is stored there: split 0 puts its tree tile in
   // stage 1 and its queries in stage 0 (one more barrier before tile 0 takes
@@ -450,6 +664,9 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   char* qbuf = sp == 0 ? stage0 : stage1;
   store_tree_tile(stage1, qbuf, TR, t_real, p.scale * kLog2e, sp == 0, tid);
   lds_sync();
+  WaveState st;
+  reset(st);
+  const LaneOffs L = lane_offsets(lane, th, kKBytes);
   u32x4 qf[8];
   load_q_frags(qf, qbuf, q, g);
   if (sp == 0) {  // uniform

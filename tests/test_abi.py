@@ -291,11 +291,18 @@ def test_plan_info_follows_flags(lib):
 
 
 def test_one_node_trees_take_the_decode_kernel(lib):
-    """t_max == 1 (bf16, head_dim 128): the decode kernel, whole contexts, no
-    workspace; the MFMA flags and the plain flag still force their kernels."""
+    """t_max == 1 (bf16, head_dim 128): the decode kernel (whole contexts, no
+    workspace) up to a 1024-token bound or when forced, the grid kernel
+    above; the MFMA flags and the plain flag still force their kernels."""
     out = [ctypes.c_int32() for _ in range(3)]
     refs = [ctypes.byref(x) for x in out]
+    desc = _desc(t_max=1, max_ctx_len=1024, max_blocks_per_seq=260, rope_max_pos=4064)
+    assert lib.tree_attn_plan_info(ctypes.byref(desc), *refs) == 0
+    assert out[0].value == 3 and out[1].value == 1 and out[2].value >= 1024
+    assert lib.tree_attn_workspace_size(ctypes.byref(desc)) == 0
     desc = _desc(t_max=1, max_ctx_len=4000, max_blocks_per_seq=260, rope_max_pos=4064)
+    assert lib.tree_attn_plan_info(ctypes.byref(desc), *refs) == 0 and out[0].value == 1
+    desc = _desc(t_max=1, max_ctx_len=4000, max_blocks_per_seq=260, rope_max_pos=4064, flags=8)
     assert lib.tree_attn_plan_info(ctypes.byref(desc), *refs) == 0
     assert out[0].value == 3 and out[1].value == 1 and out[2].value >= 4000
     assert lib.tree_attn_workspace_size(ctypes.byref(desc)) == 0

@@ -25,7 +25,10 @@ from tests._helpers import ATOL, check_attention_rows, dev, oracle_verify_rows, 
 
 pytestmark = pytest.mark.gpu
 
-def _run(wl, flags=0):
+DECODE = 8  # TA_FLAG_DECODE_KERNEL
+
+
+def _run(wl, flags=DECODE):
     d = dev(wl)
     tv = verifier(wl, flags=flags)
     from medusa_tree_attention_attn_amd._lib import tree_attn_plan_info
@@ -101,8 +104,11 @@ def test_decode_padding_root_gives_zero_row():
     _check(got, oracle_verify_rows(wl, [0, 1, 2]), wl, [0, 1, 2])
 
 
-@pytest.mark.parametrize("flags", [2, 4, 1])
+@pytest.mark.parametrize("flags", [0, 2, 4, 1])
 def test_decode_agrees_with_tree_kernels(flags):
+    """The decode kernel against the grid kernel's small-tree path (the
+    default for a 1500-token bound, and forced), the persistent and the
+    plain kernel."""
     wl = make_workload("decode_b64", 11, batch=4, heads=3, ctx_range=(0, 1500))
     a, ka = _run(wl)
     b, kb = _run(wl, flags=flags)

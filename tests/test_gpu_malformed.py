@@ -43,7 +43,8 @@ def _garbage(wl, seed):
     ("vicuna7b_b16", dict(batch=5, heads=3, ctx_range=(10, 900)), 4),   # persistent kernel
     ("vicuna7b_b16", dict(batch=5, heads=3, ctx_range=(10, 900)), 1),   # plain kernel
     ("decode_b64", dict(batch=5, heads=3, ctx_range=(10, 900)), 0),     # decode kernel
-], ids=["grid", "persistent", "simple", "decode"])
+    ("decode_b64", dict(batch=5, heads=3, ctx_range=(10, 900)), 2),     # small-tree path
+], ids=["grid", "persistent", "simple", "decode", "grid-small-trees"])
 def test_garbage_device_values_are_contained(name, kw, flags):
     wl = make_workload(name, 31, **kw)
     d = dev(wl)

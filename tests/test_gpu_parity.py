@@ -206,6 +206,51 @@ def test_verify_grouped_query_heads(kernel):
     _check_rows(got, ref, wl, [0, 1])
 
 
+MIXED_SIZES = (1, 2, 4, 8, 26, 64)
+
+
+def _mixed_workload(seed0, batch, **kw):
+    """A workload whose trees take every size of MIXED_SIZES (the first seed
+    from seed0 on whose draw covers them all)."""
+    for seed in range(seed0, seed0 + 100):
+        wl = make_workload("stress_b64", seed, batch=batch, tree_sizes=MIXED_SIZES, **kw)
+        if set(wl.tree_sizes.tolist()) == set(MIXED_SIZES):
+            return wl
+    raise AssertionError("no seed covers every tree size")
+
+
+@pytest.mark.parametrize("kernel", ["default", "persistent", "simple"])
+@pytest.mark.parametrize("split_tokens", [0, 128])
+@pytest.mark.parametrize("ctx_range", [(0, 700), (0, 20)])
+def test_verify_mixed_tree_sizes(kernel, split_tokens, ctx_range):
+    """Trees of 1, 2, 4, 8, 26 and 64 nodes side by side in one batch.  The
+    grid kernel routes each work item on the device: trees of at most 4 real
+    nodes to its vector-ALU small-tree path, the others to the matrix cores;
+    with 128-token splits the small-tree path leaves split partials for the
+    merge kernel.  Contexts ending mid-page, and of 0..20 tokens (empty and
+    sub-page contexts)."""
+    wl = _mixed_workload(40, 18, heads=4, ctx_range=ctx_range)
+    print(f"mixed trees {sorted(wl.tree_sizes.tolist())} kernel={kernel} split={split_tokens}",
+          flush=True)
+    got = _verify_gpu(wl, flags=KERNEL_FLAGS[kernel], split_tokens=split_tokens)
+    seqs = list(range(wl.spec.batch))
+    _check_rows(got, oracle_verify_rows(wl, seqs), wl, seqs)
+
+
+def test_verify_mixed_tree_sizes_grouped_query_heads():
+    """The small-tree path with 8 query heads over 2 KV heads."""
+    import dataclasses
+    wl = _mixed_workload(60, 12, heads=8, ctx_range=(20, 500))
+    kn = wl.k_new[:, :, ::4].contiguous()
+    vn = wl.v_new[:, :, ::4].contiguous()
+    pool = wl.kv_pages[:, :, ::4].contiguous()
+    spec = dataclasses.replace(wl.spec, kv_heads=2)
+    wl = dataclasses.replace(wl, spec=spec, k_new=kn, v_new=vn, kv_pages=pool)
+    got = _verify_gpu(wl)
+    seqs = list(range(wl.spec.batch))
+    _check_rows(got, oracle_verify_rows(wl, seqs), wl, seqs)
+
+
 @pytest.mark.parametrize("kernel", ["grid", "persistent"])
 def test_verify_invalid_page_reads_page_zero(kernel):
     """A block id outside the pool, inside a context, is never used as an
