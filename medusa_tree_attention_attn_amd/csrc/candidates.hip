@@ -14,23 +14,23 @@
 // first among equal values); key 0 is below every element.  The row is
 // taken in segments of kSegChunks 16-byte chunks per thread, held in
 // registers; elements past the row's end read as -inf and are excluded by
-// index where -inf matters.  Per segment:
-//   1. each thread finds its best element: the max value, then the smallest
-//      token holding it;
-//   2. each wavefront takes the k-th best of its 64 lanes' bests, and tau is
-//      the largest of these.  The wavefront that gives tau has k lanes whose
-//      bests are >= tau, so the segment's k best elements are all >= tau,
-//      and in every wavefront only lanes among its k best can hold anything
-//      >= tau;
-//   3. the elements >= tau (at most k lanes per wavefront times the values
-//      per lane) and the k winners of the previous segment go to an LDS
-//      list;
+// index.  Per segment:
+//   1. each thread takes the max value of its elements, each wavefront the
+//      max of its lanes' (values only: no key is built for most elements);
+//   2. tau is the k-th largest of the 16 wavefront maxima: at least k
+//      elements have values >= tau, so the segment's k best all do;
+//   3. the few threads whose max reaches tau stage their values in LDS, and
+//      the whole workgroup, one staged value per thread, puts the k winners
+//      of the previous segment and the elements >= tau on a list (slots
+//      taken with one LDS atomic per wavefront);
 //   4. the list's k best are ranked by counting, for each entry, the entries
-//      above it (rounds of workgroup max when the list is long).
-// Typical rows put a few dozen elements on the list; the bound holds for any
-// data, ties and NaN included.
+//      above it (rounds of workgroup max when the list is long, and over
+//      the staged values when it overflows its capacity).
+// Typical rows put about 10-25 elements on the list; any data, ties and NaN
+// included, gives the exact top-k.
 #include "launch.h"
 #include "mfma_tile.h"
+#include "page_stream.h"
 
 namespace ta {
 namespace {
@@ -38,6 +38,9 @@ namespace {
 constexpr int kCandThreads = 1024;  // 16 wavefronts: four per SIMD
 constexpr int kCandWaves = kCandThreads / 64;
 constexpr int kSegChunks = 4;  // 16-byte chunks per thread per segment
+constexpr int kListCap = 2048;  // list entries held in LDS
+constexpr int kRankPad = 256;   // list entries cleared per segment
+constexpr int kRankFast = 64;   // longest list ranked by eight threads per entry
 
 __device__ __forceinline__ uint64_t elem_key(float v, int i) {
   uint32_t u = __float_as_uint(v != v ? -INFINITY : v);
@@ -47,6 +50,12 @@ __device__ __forceinline__ uint64_t elem_key(float v, int i) {
 }
 
 __device__ __forceinline__ int key_token(uint64_t k) { return (int)~(uint32_t)k; }
+
+// A float's bits as an unsigned integer in the float's order (for non-NaN).
+__device__ __forceinline__ uint32_t mono_bits(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Value j of a chunk.
 template <typename S>
@@ -85,102 +94,220 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Max over the wavefront's lanes, with DPP moves within each row of 16 lanes
+// (neighbours, pairs, half-row mirror, row mirror) and the four row maxima
+// read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_move<0xB1>(x));
+  x = fmaxf(x, dpp_move<0x4E>(x));
+  x = fmaxf(x, dpp_move<0x141>(x));
+  x = fmaxf(x, dpp_move<0x140>(x));
+  auto lane_f = [](float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+  };
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 template <typename S>
 __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
     const S* __restrict__ head_logits, int V, int n_heads, int topk, CandTree tree,
     const int32_t* __restrict__ root_token, int32_t* __restrict__ cand,
     int32_t* __restrict__ parent, int32_t* __restrict__ depth, int T) {
   constexpr int kPer = 16 / sizeof(S);
-  constexpr int kSegValues = kSegChunks * kPer;           // per thread
-  constexpr int kCap = kMaxTopK * kCandWaves * kSegValues + kMaxTopK;  // list bound
-  __shared__ __align__(16) uint64_t s_list[kCap];
-  __shared__ __align__(16) uint64_t s_best[kCandThreads];
+  constexpr int kSegValues = kSegChunks * kPer;  // per thread
+  static_assert(kMaxTopK <= kCandWaves, "tau ranks the wavefront maxima");
+  __shared__ __align__(16) u32x4 s_stage[kCandThreads][kSegChunks];  // candidate threads' values
+  __shared__ __align__(16) uint64_t s_list[kListCap];
+  __shared__ int s_ct[kCandThreads];  // thread of each staged slot
+  __shared__ __align__(16) uint32_t s_wk[kCandWaves];
   __shared__ uint64_t s_red[kCandWaves];
-  __shared__ uint64_t s_tauw[kCandWaves];
   __shared__ uint64_t s_win[kMaxTopK];
-  __shared__ int s_n;
+  __shared__ int s_n, s_nct;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const S* row = head_logits + ((size_t)b * n_heads + h) * V;
   const bool vec = (V % kPer) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   const int nchunks = (V + kPer - 1) / kPer;
-
+  static_assert(kMaxTree <= kCandThreads, "node n is thread n's");
+  // This thread's node (n = tid), read in the first segment right after
+  // its row loads are issued, so that the reads' latency passes under the
+  // row's and nothing delays the row's loads.  (Nothing combines them
+  // before the end, so no wait for them comes before the wait for the row.)
+  bool has_node = false;
+  int nd_parent = 0, nd_depth = 0, nd_rank = 0;
+  int32_t root = 0;
   for (int c0 = 0, seg = 0; c0 < nchunks; c0 += kSegChunks * kCandThreads, ++seg) {
     u32x4 x[kSegChunks];
 #pragma unroll
     for (int u = 0; u < kSegChunks; ++u)
       x[u] = load_chunk(row, V, c0 + u * kCandThreads + tid, vec);
+    if (seg == 0) {
+      has_node = tid < tree.n_nodes;
+      if (has_node) {
+        nd_parent = tree.parent[tid];
+        nd_depth = tree.depth[tid];
+        nd_rank = tree.rank[tid];
+      }
+      // The root token through a vector load: a scalar load would be
+      // waited for with the kernel arguments.
+      int b_v = b;
+      asm volatile("" : "+v"(b_v));
+      if (h == 0 && tid == 0) root = root_token[b_v];
+    }
     const int first = (c0 + tid) * kPer;  // this thread's smallest token here
-    // 1. this thread's best element
+    // 1. this thread's max value (NaN ignored) and its wavefront's
     float m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kSegChunks; ++u)
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) m = fmaxf(m, chunk_value<S>(x[u], j));  // NaN ignored
-    uint64_t best;
-    if (m > -INFINITY) {
-      int bi = 0;
-#pragma unroll
-      for (int u = kSegChunks - 1; u >= 0; --u)
-#pragma unroll
-        for (int j = kPer - 1; j >= 0; --j)
-          if (chunk_value<S>(x[u], j) == m) bi = (c0 + u * kCandThreads + tid) * kPer + j;
-      best = elem_key(m, bi);
-    } else {
-      // only -inf, NaN or nothing: all equal, the smallest token wins
-      best = first < V ? elem_key(-INFINITY, first) : 0ull;
+      for (int j = 0; j < kPer; ++j) m = fmaxf(m, chunk_value<S>(x[u], j));
+    const float wm = wave_max(m);  // never NaN
+    if (lane == 0) s_wk[wv] = (mono_bits(wm) & ~0xFu) | (uint32_t)wv;
+    // The previous segment's winners take list slots 0 .. k-1.
+    const uint64_t prev_win = (seg > 0 && tid < topk) ? s_win[tid] : 0ull;
+    if (tid == 0) {
+      s_n = seg > 0 ? topk : 0;
+      s_nct = 0;
     }
-    s_best[tid] = best;
-    if (lane == 0) s_tauw[wv] = 0ull;
-    if (tid == 0) s_n = 0;
+    if (tid < kRankPad) s_list[tid] = 0ull;  // entries past a short list read as 0
     __syncthreads();
-    // 2. tau_w: the best of this wavefront's lanes with exactly k - 1 above
-    //    it (0 when fewer than k lanes have elements); tau = max over
-    //    wavefronts.  The wavefront holding that max has k lanes whose bests
-    //    are >= tau, so the segment's k best are all >= tau; in any
-    //    wavefront, only lanes among its k best reach tau.
-    int rank = 0;
-    const ulonglong2* sb = reinterpret_cast<const ulonglong2*>(s_best + 64 * wv);
-#pragma unroll 8
-    for (int q = 0; q < 32; ++q) {
-      const ulonglong2 e = sb[q];
-      rank += (e.x > best ? 1 : 0) + (e.y > best ? 1 : 0);
+    if (seg > 0 && tid < topk) s_list[tid] = prev_win;
+    // 2. tau: the k-th largest of the 16 wavefront maxima, ranked on lanes
+    //    0..15 as 32-bit keys: the value's monotone bits with the low four
+    //    replaced by the wavefront's index (unique keys), read back with the
+    //    low four cleared (never above any of the k values it stands for).
+    //    At least k elements have values >= tau, so the segment's k best all
+    //    do.  When tau is -inf (fewer than k wavefronts hold a finite value;
+    //    its key then reads back as NaN) every element is a candidate.
+    float tv;
+    {
+      const uint32_t mine = s_wk[lane & (kCandWaves - 1)];
+      int above = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kCandWaves; ++w2) above += s_wk[w2] > mine ? 1 : 0;
+      const uint64_t hit = __ballot(lane < kCandWaves && above == topk - 1);  // k <= 16: one lane
+      const uint32_t t = hit ? __builtin_amdgcn_readlane(mine, __builtin_ctzll(hit)) & ~0xFu : 0u;
+      tv = __uint_as_float((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
     }
-    if (rank == topk - 1 && best != 0ull) s_tauw[wv] = best;
-    __syncthreads();
-    uint64_t tau = 0ull;
+    const bool all = !(tv > -INFINITY);
+    // 3. candidate threads (max >= tau) stage their values in LDS, in slots
+    //    taken with one LDS atomic per wavefront ...
+    const bool is_cand = all ? first < V : m >= tv;
+    const uint64_t cb = __ballot(is_cand);
+    if (cb) {  // uniform
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_nct, __popcll(cb));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (is_cand) {
+        const int slot = base + lanes_below(cb);
+        s_ct[slot] = tid;
 #pragma unroll
-    for (int w = 0; w < kCandWaves; ++w) tau = s_tauw[w] > tau ? s_tauw[w] : tau;
-    // 3. the list: elements >= tau, then the previous segment's winners
-    if (best >= tau) {  // this thread holds elements >= tau
-      const float tv = __uint_as_float((uint32_t)(tau >> 32) & 0x80000000u
-                                           ? (uint32_t)(tau >> 32) & 0x7FFFFFFFu
-                                           : ~(uint32_t)(tau >> 32));
-      const bool exact = !(tv > -INFINITY);  // tau is -inf or none: test keys
-#pragma unroll
-      for (int u = 0; u < kSegChunks; ++u) {
-        const int i0 = (c0 + u * kCandThreads + tid) * kPer;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const float v = chunk_value<S>(x[u], j);
-          if (exact || v >= tv) {
-            const uint64_t k = elem_key(v, i0 + j);
-            if (i0 + j < V && k >= tau) {
-              const int slot = atomicAdd(&s_n, 1);
-              if (slot < kCap) s_list[slot] = k;
-            }
-          }
-        }
+        for (int u = 0; u < kSegChunks; ++u) s_stage[slot][u] = x[u];
       }
     }
-    if (seg > 0 && tid < topk) {
-      const int slot = atomicAdd(&s_n, 1);
-      if (slot < kCap) s_list[slot] = s_win[tid];
+    __syncthreads();
+    //    ... and the workgroup, one staged value per thread, puts the
+    //    elements >= tau on the list (again one atomic per wavefront).
+    const int n_vals = s_nct * kSegValues;
+    for (int e0 = wv * 64; e0 < n_vals; e0 += kCandThreads) {  // uniform per wavefront
+      const int e = e0 + lane;
+      const int slot = e / kSegValues, jj = e % kSegValues;
+      float v = -INFINITY;
+      int tok = V;
+      if (e < n_vals) {
+        const int u = jj / kPer, q = jj % kPer;
+        v = chunk_value<S>(s_stage[slot][u], q);
+        tok = (c0 + u * kCandThreads + s_ct[slot]) * kPer + q;
+      }
+      const bool ok = tok < V && (all || v >= tv);
+      const uint64_t ob = __ballot(ok);
+      if (ob) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_n, __popcll(ob));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const int at = base + lanes_below(ob);
+        if (ok && at < kListCap) s_list[at] = elem_key(v, tok);
+      }
     }
     __syncthreads();
-    // 4. the list's k best, in order
-    const int n = min(s_n, kCap);
-    if (n <= kCandThreads) {
+    // 4. the k best, in order: by counting, for each list entry, the entries
+    //    above it; rounds of workgroup max over a long list; and when the
+    //    list overflowed (rows whose values crowd at the top, e.g. all
+    //    equal), rounds of workgroup max over the staged values.
+    const int n_all = s_n;
+    auto wg_max = [&](uint64_t w) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = shfl_xor_u64(w, off);
+        w = o > w ? o : w;
+      }
+      if (lane == 0) s_red[wv] = w;
+      __syncthreads();
+      w = s_red[0];
+#pragma unroll
+      for (int q = 1; q < kCandWaves; ++q) w = s_red[q] > w ? s_red[q] : w;
+      return w;
+    };
+    if (n_all > kListCap) {
+      // Overflow: rounds over the staged values, filtered as above.
+      uint64_t prev = ~0ull;  // above every element
+      for (int r = 0; r < topk; ++r) {
+        uint64_t w = (seg > 0 && tid < topk && prev_win < prev) ? prev_win : 0ull;
+        for (int e = tid; e < n_vals; e += kCandThreads) {
+          const int slot = e / kSegValues, jj = e % kSegValues;
+          const int u = jj / kPer, q = jj % kPer;
+          const float v = chunk_value<S>(s_stage[slot][u], q);
+          const int tok = (c0 + u * kCandThreads + s_ct[slot]) * kPer + q;
+          if (tok < V && (all || v >= tv)) {
+            const uint64_t k = elem_key(v, tok);
+            if (k < prev && k > w) w = k;
+          }
+        }
+        w = wg_max(w);
+        if (tid == 0) s_win[r] = w;
+        prev = w;
+        __syncthreads();
+      }
+    } else if (n_all <= kRankFast) {
+      // Eight threads per entry, each comparing it with every eighth entry
+      // (entries n .. kRankPad - 1 are 0 and count for nothing); the eight
+      // partial counts are summed with DPP moves within each half-row.
+      const int i = tid >> 3, j0 = tid & 7;
+      const uint64_t e = s_list[i];
+      int r = 0;
+#pragma unroll
+      for (int m = 0; m < kRankFast / 8; ++m) r += s_list[j0 + 8 * m] > e ? 1 : 0;
+      r += __builtin_amdgcn_mov_dpp(r, 0xB1, 0xF, 0xF, false);   // neighbours
+      r += __builtin_amdgcn_mov_dpp(r, 0x4E, 0xF, 0xF, false);   // pairs
+      r += __builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, false);  // quads of a half-row
+      if (j0 == 0 && i < n_all && r < topk) s_win[r] = e;
+      __syncthreads();
+    } else if (n_all <= kRankPad - 8) {
+      // Eight entries per step: entries n .. kRankPad - 1 are 0 and count
+      // for nothing.
+      const int n = n_all;
+      if (tid < n) {
+        const uint64_t e = s_list[tid];
+        int r = 0;
+        const ulonglong2* sl = reinterpret_cast<const ulonglong2*>(s_list);
+        for (int q = 0; q < n; q += 8) {
+          ulonglong2 p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = sl[q / 2 + i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r += (p[i].x > e ? 1 : 0) + (p[i].y > e ? 1 : 0);
+        }
+        if (r < topk) s_win[r] = e;
+      }
+      __syncthreads();
+    } else if (n_all <= kCandThreads) {
+      const int n = n_all;
       if (tid < n) {
         const uint64_t e = s_list[tid];
         int r = (n & 1) && s_list[n - 1] > e ? 1 : 0;
@@ -193,6 +320,7 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
       }
       __syncthreads();
     } else {
+      const int n = n_all;
       uint64_t prev = ~0ull;  // above every element
       for (int r = 0; r < topk; ++r) {
         uint64_t w = 0ull;
@@ -200,16 +328,7 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
           const uint64_t e = s_list[q];
           if (e < prev && e > w) w = e;
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          const uint64_t o = shfl_xor_u64(w, off);
-          w = o > w ? o : w;
-        }
-        if (lane == 0) s_red[wv] = w;
-        __syncthreads();
-        w = s_red[0];
-#pragma unroll
-        for (int q = 1; q < kCandWaves; ++q) w = s_red[q] > w ? s_red[q] : w;
+        w = wg_max(w);
         if (tid == 0) s_win[r] = w;
         prev = w;
         __syncthreads();
@@ -219,15 +338,13 @@ __global__ __launch_bounds__(kCandThreads) void candidates_kernel(
 
   // Nodes at depth h + 1 take their rank's token.
   const size_t base = (size_t)b * T;
-  for (int n = tid; n < tree.n_nodes; n += kCandThreads) {
-    if (n > 0 && tree.depth[n] == h + 1) cand[base + n] = key_token(s_win[tree.rank[n]]);
-  }
+  if (has_node && tid > 0 && nd_depth == h + 1) cand[base + tid] = key_token(s_win[nd_rank]);
   if (h == 0) {
     for (int n = tid; n < T; n += kCandThreads) {
-      if (n < tree.n_nodes) {
-        parent[base + n] = tree.parent[n];
-        depth[base + n] = tree.depth[n];
-        if (n == 0) cand[base] = root_token[b];
+      if (n < tree.n_nodes) {  // n == tid
+        parent[base + n] = nd_parent;
+        depth[base + n] = nd_depth;
+        if (n == 0) cand[base] = root;
       } else {
         parent[base + n] = kPadParent;
         depth[base + n] = 0;

@@ -83,10 +83,11 @@ def test_prepared_table_reused_across_calls():
 
 
 def test_candidates_adversarial_rows():
-    """Rows whose best values all sit in a few threads' share of the row,
-    rows that put thousands of elements on the candidate list (the rounds
-    path), all-equal rows (ties decided by token), rows of -inf and NaN, and
-    a +inf."""
+    """Rows whose best values all sit in a few threads' share of the row (a
+    list of hundreds), all-equal rows (ties decided by token; the list
+    overflows and the staged values are searched), rows of -inf and NaN with
+    one +inf (tau is -inf: every element is a candidate), and rows whose
+    wavefront maxima are all equal (lists longer than the workgroup)."""
     B, H, V, topk = 1, 4, 32000, 16
     choices = make_choices(9, n=60, max_depth=4, topk=topk)
     x = make_head_logits(B, H, V, seed=9, dtype=torch.float32)
@@ -100,14 +101,15 @@ def test_candidates_adversarial_rows():
     x[0, 2, 7] = float("inf")
     x[0, 3, ::3] = float("nan")
     logits = x.to(torch.bfloat16)
-    # Head 3 of a second sequence: lanes 0..15 of every wavefront hold values
-    # 100 + lane (16-byte chunk c = token // 8 goes to thread c % 1024, lane =
-    # thread % 64), so every wavefront's 16th-best lane is at 100 and about
-    # 15 x 32 elements per wavefront reach the bound: a list far longer than
-    # the workgroup (the rounds path).
+    # A second sequence: the 16-byte chunk c = token // 8 goes to thread
+    # c % 1024, lane = thread % 64.  Head 3: lanes 0..15 of every wavefront
+    # hold 100 + lane, so every wavefront's max is 115 and the list holds the
+    # ~500 elements at 115.  Head 2: lanes 0..2 hold 100, so the list holds
+    # ~1500 equal elements (longer than the workgroup: rounds over the list).
     y = make_head_logits(1, H, V, seed=19, dtype=torch.float32)
     lane_of = (idx // 8) % 1024 % 64
     y[0, 3] = torch.where(lane_of < 16, 100.0 + lane_of.float(), y[0, 3])
+    y[0, 2] = torch.where(lane_of < 3, torch.full_like(y[0, 2], 100.0), y[0, 2])
     logits = torch.cat([logits, y.to(torch.bfloat16)], dim=0)
     B = 2
     root = torch.tensor([4, 9], dtype=torch.int32)
