@@ -21,8 +21,10 @@ namespace {
 
 constexpr int kArgThreads = 256;  // threads per logits row (argmax)
 // Threads per logits row of the entropy pass (16 x 64 rows of 32000 bf16,
-// with two chunks per batch: 18.5 us at 256 threads, 18.8 at 512; with one
-// chunk per batch 19.4, 20.1 and 23.5 at 256, 512 and 1024).
+// with a running max and two chunks per batch: 18.5 us at 256 threads, 18.8
+// at 512; with one chunk per batch 19.4, 20.1 and 23.5 at 256, 512 and
+// 1024.  With a fixed reference: 17.0 us at 256 and at 512 threads, and the
+// same with all of a thread's chunks in flight at once).
 constexpr int kEntThreads = 256;
 
 struct Best {
@@ -156,17 +158,22 @@ __global__ __launch_bounds__(kArgThreads) void vocab_argmax_kernel(const S* __re
 // of n passes iff p[cand_tokens[c]] > min(epsilon, delta * exp(-H)).
 //
 // Kernel 1, one workgroup per (sequence, node) row, one pass over the row in
-// base 2: with u = x * log2(e) / temperature, every thread keeps the running
-// max m of u, z = sum 2^(u - m) and s = sum 2^(u - m) (u - m).  Each batch
-// of two 16-byte chunks per thread (stream_row) is held in registers, so its
-// max is taken first and the batch adds to (m, z, s) with one rescale
-// (2^(m - m') when the max moves to m').  Since e^(y - M) = 2^(u - m) and
-// y - M = (u - m) ln 2 for y = x / temperature and its max M,
-//   lse = (m + log2 z) ln 2,   H = ln z - sum e^(y - M) (y - M) / z
+// base 2: with u = x * log2(e) / temperature, every thread keeps a
+// reference m (a value of u it has seen), z = sum 2^(u - m) and
+// s = sum 2^(u - m) (u - m), over batches of two 16-byte chunks per thread
+// (stream_row); the threads' states are merged with rescales (2^(m - m')
+// when the reference moves to m').  Since e^(y - m ln 2) = 2^(u - m) for
+// y = x / temperature, whatever the reference,
+//   lse = (m + log2 z) ln 2,   H = ln z - sum e^(y - m ln 2) (y - m ln 2) / z
 //                                = (log2 z - s / z) ln 2.
 // Kernel 2, one wavefront per sequence: each child gathers its token's logit
 // from the parent's row and tests p = e^(x / temperature - lse) against the
 // threshold; the path is then chosen as in greedy acceptance.
+// Measured on 16 x 64 rows of 32000 bf16 (graph replay): 17.1 us for both
+// launches; 14.5 us for kernel 1 alone, 12.4 us for kernel 1 with nothing
+// but its loads (65.5 MB: 5.3 TB/s with the launch and first-load latency
+// included), so the row pass is close to its read floor and the second
+// launch (two dependent round trips) costs 2.7 us.
 // ---------------------------------------------------------------------------
 struct Lse {
   float m, z, s;  // base-2 running max, sum of 2^(u - m), sum of 2^(u - m) (u - m)
@@ -202,9 +209,16 @@ __device__ __forceinline__ void add_term(Lse& t, float x, float c) {
   t.s = fmaf(e, d, t.s);
 }
 
-// Entropy consumer of stream_row: each batch of chunks is reduced
-// against its own max (c > 0, so the max of x is also the max of u = x c)
-// and merged into the running state with one rescale.
+// Entropy consumer of stream_row.  Each thread sums its terms against a
+// reference it fixes once: the max of its first batch holding a finite
+// value (c > 0, so the max of x gives the max of u = x c).  A batch then
+// adds its sums to the running ones with no max pass and no rescale; the
+// identities for lse and H hold for any reference.  A batch whose sum
+// reaches 2^32 (a value 32 or more above the reference in base 2, or +inf)
+// is redone against its own max and merged with a rescale, which moves the
+// reference up; so terms stay below 2^32 and the reference within 32 of
+// the values that carry the mass.  A batch with no finite max adds nothing
+// (as a batch whose max is +inf gives no finite term).
 template <typename S>
 struct EntropyOp {
   static constexpr int kBatch = 2;
@@ -212,7 +226,7 @@ struct EntropyOp {
   Lse a;
   float c;
   int nchunks, tid;
-  __device__ __forceinline__ void batch(const u32x4 (&x)[kBatch], int i0) {
+  __device__ __forceinline__ float batch_max(const u32x4 (&x)[kBatch], int i0) const {
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -223,8 +237,9 @@ struct EntropyOp {
                               : fmaxf(mx, __uint_as_float(x[u][w]));
       }
     }
-    if (mx == -INFINITY) return;  // nothing but -inf (or no values): no mass
-    Lse t{mx * c, 0.f, 0.f};
+    return mx;
+  }
+  __device__ __forceinline__ void terms(Lse& t, const u32x4 (&x)[kBatch], int i0) const {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if ((i0 + u) * kThreads + tid < nchunks) {
@@ -239,7 +254,24 @@ struct EntropyOp {
         }
       }
     }
-    merge_lse(a, t);
+  }
+  __device__ __forceinline__ void batch(const u32x4 (&x)[kBatch], int i0) {
+    if (a.z == 0.f) {  // no reference yet
+      const float mx = batch_max(x, i0);
+      if (!(fabsf(mx) < INFINITY)) return;
+      a.m = mx * c;
+    }
+    Lse t{a.m, 0.f, 0.f};
+    terms(t, x, i0);
+    if (t.z < 0x1p32f) {
+      a.z += t.z;
+      a.s += t.s;
+      return;
+    }
+    const float mx = batch_max(x, i0);
+    Lse r{mx * c, 0.f, 0.f};
+    terms(r, x, i0);
+    merge_lse(a, r);
   }
 };
 
