@@ -68,6 +68,7 @@ def counted_traffic(workload: str, kernel: str):
 VERIFY_SOURCES = [
     "medusa_tree_attention_attn_amd/csrc/verify_mfma.hip",
     "medusa_tree_attention_attn_amd/csrc/mfma_tile.h",
+    "medusa_tree_attention_attn_amd/csrc/page_stream.h",
     "medusa_tree_attention_attn_amd/csrc/common.h",
 ]
 
