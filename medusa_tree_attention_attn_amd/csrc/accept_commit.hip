@@ -28,12 +28,11 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // KV commit (mlc-llm issue #2319 KV-cache update; vLLM issue #1171 block
-// tables): one workgroup per (path slot i, sequence b).  Slot i < accept_len
-// takes node n = accept_path[i] to position p = ctx_len + i: page
-// block_table[p / 16], row p % 16.  K is rotated at p with the fixed-order
-// fp32 arithmetic and rounded to the pool type; V is copied bit for bit.
-// Each thread handles 8 consecutive RoPE pairs with 16-byte loads, all issued
-// before any use, so a slot costs about one memory round trip.
+// tables): slot i < accept_len takes node n = accept_path[i] to position
+// p = ctx_len + i: page block_table[p / 16], row p % 16.  K is rotated at p
+// with the fixed-order fp32 arithmetic and rounded to the pool type; V is
+// copied bit for bit.  The 16-byte row helpers below serve the commit
+// kernels further down.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
