@@ -160,6 +160,22 @@ __device__ __forceinline__ void load_tree_rope(TreeRaw& TR, const float* rope, i
   for (int i = 0; i < 8; ++i) TR.cs[i] = cs[i];
 }
 constexpr int kQRow = 256 + 16;  // query buffer row (padded as the K rows)
+
+// The (cos, sin) rows of positions ctx .. ctx + kRopeRows - 1 (tree depths
+// 0 .. kRopeRows - 1) are staged in LDS during round trip 1, when the
+// launch ranking has already read ctx_len, so that the tree tile and the
+// queries can be rotated as soon as round trip 1 is back; trees with deeper
+// nodes read their rows from the table in round trip 2.  They sit in stage 0
+// after the query buffer, which no context tile takes before the rotation.
+constexpr int kRopeRows = 8;
+constexpr int kRopeRowBytes = kD * 4;
+constexpr int kRopeOff = kTile * kQRow;
+__device__ __forceinline__ void read_tree_rope_lds(TreeRaw& TR, const char* rope_lds, int row,
+                                                   int tid) {
+  const f32x4* cs = reinterpret_cast<const f32x4*>(rope_lds + row * kRopeRowBytes) + 8 * (tid & 3);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) TR.cs[i] = cs[i];
+}
 __device__ __forceinline__ void store_tree_tile(char* stage, char* qbuf, const TreeRaw& TR,
                                                 int t_real, float qscale, bool with_kv, int tid) {
   const int j = tid >> 2, u = tid & 3;
@@ -305,6 +321,17 @@ __device__ __forceinline__ void write_partial_half(const WaveState& st, const Ve
   if (write_ml && g == 0) p.ws_ml[row] = float2{st.m, st.l};
 }
 
+// What round trip 1 of a work item leaves: its context bounds, and the
+// tree structure with one lane per node (every wavefront computes it).
+struct ItemMeta {
+  int ctx, nsplit, c1, npages;
+  int t_real;     // real nodes (a prefix of the rows)
+  uint64_t anc;   // ancestor-or-self bitmask of node `lane`
+  int dep;        // depth of node `lane`
+  int pos_j;      // position of node tid/4: ctx + its depth
+  bool rope_lds;  // this wavefront's nodes take their (cos, sin) rows from LDS
+};
+
 // ---------------------------------------------------------------------------
 // Small trees (at most kSmallTree = 2 real nodes, e.g. the one-node rows of
 // a mixed batch where speculation is off for some sequences): a 32-query
@@ -335,18 +362,21 @@ constexpr int kSmallTree = 2;
 
 template <int kM>
 __device__ __forceinline__ void small_tree_item(const VerifyParams& p, const Geo& G, TreeRaw& TR,
-                                                int pos_j, char* smem, int n_tiles, int c0,
-                                                int c1, int b, int h, int sp, int nsplit,
-                                                int t_real, uint64_t anc, int tid) {
+                                                const ItemMeta& M, char* smem, int n_tiles,
+                                                int c0, int b, int h, int sp, int tid) {
   const int lane = tid & 63, wv = tid >> 6, grp = lane >> 4, dc = lane & 15;
   const int T = p.T;
-  // Round trip 2 as on the matrix-core path: the (cos, sin) rows and context
-  // tiles 0 and 1; the rotated queries go to stage 0, the tree tile to
-  // stage 1 (no context tile goes through LDS here).
-  load_tree_rope(TR, p.rope, pos_j, tid);
+  const int c1 = M.c1, nsplit = M.nsplit, t_real = M.t_real;
+  const uint64_t anc = M.anc;
+  // Round trip 2 as on the matrix-core path: context tiles 0 and 1 (and the
+  // (cos, sin) rows when they are not in LDS); the rotated queries go to
+  // stage 0, the tree tile to stage 1 (no context tile goes through LDS
+  // here).
+  if (!M.rope_lds) load_tree_rope(TR, p.rope, M.pos_j, tid);  // uniform per wavefront
   TileRegs R0, R;
   load_ctx_tile(R0, G, c0, tid);
   load_ctx_tile(R, G, c0 + kTile, tid);
+  if (M.rope_lds) read_tree_rope_lds(TR, smem + kRopeOff, M.pos_j - M.ctx, tid);
   const char* qbuf = smem;
   const char* tree_stage = smem + kStageBytes;
   store_tree_tile(smem + kStageBytes, smem, TR, t_real, p.scale * kLog2e, sp == 0, tid);
@@ -464,15 +494,6 @@ __device__ __forceinline__ void small_tree_item(const VerifyParams& p, const Geo
   }
 }
 
-// What round trip 1 of a work item leaves: its context bounds, and the
-// tree structure with one lane per node (every wavefront computes it).
-struct ItemMeta {
-  int ctx, nsplit, c1, npages;
-  int t_real;     // real nodes (a prefix of the rows)
-  uint64_t anc;   // ancestor-or-self bitmask of node `lane`
-  int dep;        // depth of node `lane`
-  int pos_j;      // position of node tid/4: ctx + its depth
-};
 
 // ---- Round trip 1: ctx_len, page ids, tree rows, then the q rows and the
 // tree k/v rows.  Every load is unconditional (row indices clamped into
@@ -482,8 +503,9 @@ struct ItemMeta {
 // tree k/v rows stay in flight into round trip 2).  Returns false (uniform)
 // when the split lies beyond the context.
 __device__ __forceinline__ bool item_round_trip1(const VerifyParams& p, int b, int h, int hk,
-                                                 int sp, int c0, int* s_pages, TreeRaw& TR,
-                                                 ItemMeta& M, int tid) {
+                                                 int sp, int c0, int ctx0, char* rope_lds,
+                                                 int* s_pages, TreeRaw& TR, ItemMeta& M,
+                                                 int tid) {
   const int lane = tid & 63;
   const int T = p.T;
   const int ctx_raw = p.ctx_lens[b];
@@ -497,6 +519,12 @@ __device__ __forceinline__ bool item_round_trip1(const VerifyParams& p, int b, i
   const int row_l = min(lane, T - 1);
   const int par_raw = p.tree_parent[(size_t)b * T + row_l];
   const int dep_raw = p.tree_depth[(size_t)b * T + row_l];
+  // The (cos, sin) rows ctx0 .. ctx0 + kRopeRows - 1, 16 bytes per thread
+  // (ctx0 < 0, ctx_len not known at launch: rows from 0, not used).
+  static_assert(kRopeRows * kRopeRowBytes == 16 * kThreads, "one chunk per thread");
+  const int rope_row = min(max(ctx0, 0) + (tid >> 5), p.rope_max_pos - 1);
+  const u32x4 rope_chunk =
+      *reinterpret_cast<const u32x4*>(p.rope + (size_t)rope_row * kD + 4 * (tid & 31));
   // Every split rotates its queries; only split 0 uses the tree k/v rows (the
   // others read row 0 over and over).
   load_tree_raw(TR, p, b, h, hk, sp == 0 ? T - 1 : 0, tid);
@@ -512,6 +540,7 @@ __device__ __forceinline__ bool item_round_trip1(const VerifyParams& p, int b, i
     s_pages[tid] = (tid < M.npages && blk_raw0 >= 0 && blk_raw0 < p.num_blocks) ? blk_raw0 : 0;
   if (tid + kThreads < M.npages)
     s_pages[tid + kThreads] = (blk_raw1 >= 0 && blk_raw1 < p.num_blocks) ? blk_raw1 : 0;
+  *reinterpret_cast<u32x4*>(rope_lds + 16 * tid) = rope_chunk;
   const int par = lane < T ? par_raw : kPadParent;
   M.dep = lane < T ? dep_raw : 0;
 
@@ -529,29 +558,31 @@ __device__ __forceinline__ bool item_round_trip1(const VerifyParams& p, int b, i
     up = up_up;
   }
   M.anc = anc;
-  M.pos_j = M.ctx + clampi(__shfl(M.dep, tid >> 2), 0, T - 1);
+  const int dj = clampi(__shfl(M.dep, tid >> 2), 0, T - 1);
+  M.pos_j = M.ctx + dj;
+  M.rope_lds = ctx0 == M.ctx && __ballot((tid >> 2) < M.t_real && dj >= kRopeRows) == 0ull;
   return true;
 }
 
 // A work item whose tree has at most kSmallTree real nodes: round trip 1 as
 // on the matrix-core path, then the vector-ALU path above.
 __device__ __forceinline__ void small_tree_workgroup(const VerifyParams& p, int b, int h, int sp,
-                                                     char* smem, int* s_pages, int tid) {
+                                                     int ctx0, char* smem, int* s_pages,
+                                                     int tid) {
   const int hk = h / (p.H / p.Hkv);
   const int c0 = sp * p.chunk;
   TreeRaw TR;
   ItemMeta M;
-  if (!item_round_trip1(p, b, h, hk, sp, c0, s_pages, TR, M, tid)) return;  // uniform
+  if (!item_round_trip1(p, b, h, hk, sp, c0, ctx0, smem + kRopeOff, s_pages, TR, M, tid))
+    return;  // uniform
   lds_sync();  // s_pages visible
   const Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv,
               max(M.npages - 1, 0)};
   const int n_tiles = (M.c1 - c0 + kTile - 1) / kTile;
   if (M.t_real <= 1)
-    small_tree_item<1>(p, G, TR, M.pos_j, smem, n_tiles, c0, M.c1, b, h, sp, M.nsplit, M.t_real,
-                       M.anc, tid);
+    small_tree_item<1>(p, G, TR, M, smem, n_tiles, c0, b, h, sp, tid);
   else
-    small_tree_item<2>(p, G, TR, M.pos_j, smem, n_tiles, c0, M.c1, b, h, sp, M.nsplit, M.t_real,
-                       M.anc, tid);
+    small_tree_item<2>(p, G, TR, M, smem, n_tiles, c0, b, h, sp, tid);
 }
 
 // Launch slot -> (sequence, head, split).  A (sequence, split) group holds H
@@ -567,9 +598,10 @@ __device__ __forceinline__ void small_tree_workgroup(const VerifyParams& p, int 
 // frees up first.  With more than 64 groups the order is (sequence, head)
 // major, split minor.  Every lane of the wavefront takes part (lane = group).
 __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int lane, int& b,
-                                            int& h, int& sp, bool& small) {
+                                            int& h, int& sp, bool& small, int& ctx0) {
   const int G = p.B * p.splits;
   small = false;
+  ctx0 = -1;
   if (G > 64 || p.n_cu <= 0) {
     b = (slot / p.splits) / p.H;
     h = (slot / p.splits) % p.H;
@@ -578,11 +610,13 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
   }
   int len = -1;  // tokens of the group's split; -1: the split does not exist
   int small_l = 0;  // the group's tree has at most kSmallTree real nodes
+  int ctx_l = 0;    // the group's ctx_len (clamped)
   if (lane < G) {
     const int j = lane / p.splits, s = lane - j * p.splits;
     const int ctx_raw = p.ctx_lens[j];
     const int par_cut = p.tree_parent[(size_t)j * p.T + min(kSmallTree, p.T - 1)];
     const int c = clampi(ctx_raw, 0, p.max_ctx);
+    ctx_l = c;
     const int n = c == 0 ? 1 : (c + p.chunk - 1) / p.chunk;
     if (s < n) len = min(p.chunk, c - s * p.chunk);
     // Real nodes form a prefix, so a padding node at index kSmallTree (or a
@@ -605,6 +639,7 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
   b = grp / p.splits;
   sp = grp - b * p.splits;
   small = __shfl(small_l, grp) != 0;
+  ctx0 = __shfl(ctx_l, grp);
   return true;
 }
 
@@ -619,9 +654,11 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   const int g = lane >> 5, r32 = lane & 31;
   int b, h, sp;
   bool small;
-  if (!launch_item(p, blockIdx.x, lane, b, h, sp, small)) return;
+  int ctx0;  // ctx_len read by the launch ranking (-1: not read)
+  if (!launch_item(p, blockIdx.x, lane, b, h, sp, small, ctx0)) return;
+  static_assert(kRopeOff + kRopeRows * kRopeRowBytes <= kStageBytes, "rope rows in stage 0");
   if (small) {  // uniform: a tree of at most kSmallTree real nodes
-    small_tree_workgroup(p, b, h, sp, smem, s_pages, tid);
+    small_tree_workgroup(p, b, h, sp, ctx0, smem, s_pages, tid);
     return;
   }
   const int bh = b * p.H + h;
@@ -632,7 +669,8 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
 
   TreeRaw TR;
   ItemMeta M;
-  if (!item_round_trip1(p, b, h, hk, sp, c0, s_pages, TR, M, tid)) return;  // uniform
+  if (!item_round_trip1(p, b, h, hk, sp, c0, ctx0, smem + kRopeOff, s_pages, TR, M, tid))
+    return;  // uniform
   const int ctx = M.ctx, nsplit = M.nsplit, c1 = M.c1, npages = M.npages, t_real = M.t_real;
   const uint64_t anc = M.anc;
   const int pos_j = M.pos_j;
@@ -647,11 +685,14 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   // tiles load.
   Geo G{static_cast<const uint16_t*>(p.kv_pages), s_pages, c0, hk, p.Hkv, max(npages - 1, 0)};
   const int n_tiles = (c1 - c0 + kTile - 1) / kTile;
-  load_tree_rope(TR, p.rope, pos_j, tid);  // node tid/4's row: its key and its query
+  // Node tid/4's (cos, sin) row, for its key and its query: from LDS, or
+  // (deep trees) from the table before the tiles are issued.
+  if (!M.rope_lds) load_tree_rope(TR, p.rope, pos_j, tid);  // uniform per wavefront
   TileRegs R0;  // context tile 0
   TileRegs R;   // context tile t + 1 while tile t is computed
   load_ctx_tile(R0, G, c0, tid);  // unconditional: the compiler counts the loads
   load_ctx_tile(R, G, c0 + kTile, tid);
+  if (M.rope_lds) read_tree_rope_lds(TR, smem + kRopeOff, pos_j - ctx, tid);
 
   char* stage0 = smem;
   char* stage1 = smem + kStageBytes;
