@@ -627,9 +627,12 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
   if (slot >= N) return false;  // uniform
   int r = slot;
   if (N > p.n_cu && N <= 2 * p.n_cu && slot >= p.n_cu) r = N - 1 - (slot - p.n_cu);
+  // Each lane counts the groups ranked above its own; group j's length is
+  // read from lane j with a lane read (a lane shuffle would take a round
+  // trip through the LDS crossbar per group).
   int rank = 0;
-  for (int j = 0; j < G; ++j) {
-    const int lj = __shfl(len, j);
+  for (int j = 0; j < G; ++j) {  // uniform
+    const int lj = __builtin_amdgcn_readlane(len, j);
     rank += (lj > len) || (lj == len && j < lane);
   }
   const int gr = r / p.H;
@@ -638,8 +641,8 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
   const int grp = hit ? __builtin_ctzll(hit) : 0;
   b = grp / p.splits;
   sp = grp - b * p.splits;
-  small = __shfl(small_l, grp) != 0;
-  ctx0 = __shfl(ctx_l, grp);
+  small = __builtin_amdgcn_readlane(small_l, grp) != 0;
+  ctx0 = __builtin_amdgcn_readlane(ctx_l, grp);
   return true;
 }
 
