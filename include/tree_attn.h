@@ -25,9 +25,11 @@
  * Conventions shared by every call
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
- *    contiguous, 16-byte aligned (the kernels move 16-byte vectors).  The library allocates nothing, keeps no global state, never
- *    synchronises the device with the host, and enqueues all work on
- *    desc->stream (a hipStream_t; NULL = the default stream).
+ *    contiguous, 16-byte aligned (the kernels move 16-byte vectors).  The
+ *    library allocates nothing, keeps no global state besides the static
+ *    device workspace of tree_attn_verify_noalloc, never synchronises the
+ *    device with the host, and enqueues all work on desc->stream (a
+ *    hipStream_t; NULL = the default stream).
  *  - Element type of q, k_new, v_new, kv_pages and out is desc->dtype
  *    (TA_BF16 or TA_F32); index tensors are int32.
  *  - Layouts (B = batch, T = t_max, H = num_heads, Hkv = num_kv_heads,

@@ -224,7 +224,7 @@ def _mixed_workload(seed0, batch, **kw):
 @pytest.mark.parametrize("ctx_range", [(0, 700), (0, 20)])
 def test_verify_mixed_tree_sizes(kernel, split_tokens, ctx_range):
     """Trees of 1, 2, 4, 8, 26 and 64 nodes side by side in one batch.  The
-    grid kernel routes each work item on the device: trees of at most 4 real
+    grid kernel routes each work item on the device: trees of at most 2 real
     nodes to its vector-ALU small-tree path, the others to the matrix cores;
     with 128-token splits the small-tree path leaves split partials for the
     merge kernel.  Contexts ending mid-page, and of 0..20 tokens (empty and
