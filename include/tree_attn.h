@@ -354,8 +354,9 @@ int tree_attn_rope_table(int32_t head_dim, float base, int32_t max_pos, float* t
 /* Read-bandwidth probe (measurement only; no step of the method calls it).
  * Streams the first bytes/16*16 bytes of the device buffer src with the load
  * width (16 bytes per lane) and cache policy (non-temporal) of the
- * tree-verify kernels' KV stream, and XORs them into the device word *sink
- * (4-byte aligned; its value is meaningless, it only keeps the loads live).
+ * tree-verify kernels' KV stream, and XORs every 32-bit word it reads into
+ * the device word *sink (4-byte aligned): *sink ^= the XOR of those words,
+ * which keeps the loads live and shows that each word was read once.
  * Timing this call on a buffer larger than the 256 MB Infinity Cache gives
  * the rate at which the device at hand streams a read-only buffer: the
  * practical ceiling beside the 8 TB/s nominal peak.  src 16-byte aligned.
