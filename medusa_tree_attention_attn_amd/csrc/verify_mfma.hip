@@ -743,11 +743,18 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   }
 
   // Merge the two token halves of each query tile; each wavefront of the
-  // pair finishes two of the four d-tiles.
-  __syncthreads();
+  // pair finishes two of the four d-tiles.  The halves are parked in the
+  // stage that the last tile did not use (every wavefront passed a barrier
+  // after its last read of it), so no barrier comes first; the output tile
+  // then takes the last tile's stage, free after the barrier that follows
+  // the parking.
+  char* last_stage = (n_tiles == 0 || ((n_tiles - 1) & 1)) ? stage1 : stage0;
+  char* free_stage = last_stage == stage0 ? stage1 : stage0;
+  static_assert(4 * kHalfPark * sizeof(float) <= kStageBytes, "park area in a stage");
+  static_assert(kTile * kOutRow <= kStageBytes, "output tile in a stage");
   // (th is uniform over a wavefront: each branch indexes the accumulators
   // with constants.)
-  float* park = reinterpret_cast<float*>(smem);
+  float* park = reinterpret_cast<float*>(free_stage);
   if (active) {
     if (th == 0)
       park_half<2>(st, park + (2 * qt) * kHalfPark, lane);
@@ -763,9 +770,7 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
     st.l += __shfl_xor(st.l, 32);
   }
   if (nsplit == 1) {  // uniform
-    static_assert(4 * kHalfPark * sizeof(float) + kTile * kOutRow <= 2 * kStageBytes,
-                  "output tile after the park area");
-    char* tile = smem + 4 * kHalfPark * sizeof(float);
+    char* tile = last_stage;
     if (th == 0)
       stage_out<0>(st, tile, q, row_real, g);
     else
