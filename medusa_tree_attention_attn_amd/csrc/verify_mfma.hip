@@ -29,10 +29,12 @@
 //     will store them, masked by per-node ancestor bitmasks built with
 //     pointer doubling across the lanes of a wavefront.
 // Splits of one (b, h) leave (m, l, O) partials in the workspace; a second,
-// small kernel merges them.  The prologue takes two dependent memory round
-// trips: everything that does not depend on ctx_len (page ids, tree rows, q
-// row, tree k/v rows), then the (cos, sin) rows and the first two context
-// tiles; the tree tile is built and computed while those tiles load.
+// small kernel merges them.  The prologue takes three dependent memory round
+// trips: the launch ranking (every sequence's ctx_len, and the tree row that
+// marks small trees), then the work item's page ids, tree rows, q rows and
+// tree k/v rows with the (cos, sin) rows of depths 0-7 (ctx_len is known by
+// then), then the first two context tiles; the queries and the tree tile are
+// rotated and the tree tile is computed while those tiles load.
 #include "launch.h"
 #include "mfma_tile.h"
 #include "page_stream.h"
