@@ -351,7 +351,7 @@ struct ItemMeta {
 // wavefront w, group g), masked by each query's ancestor bitmask.  The 16
 // states of each query are merged through LDS at the end.  The item is
 // routed here at launch (the tree row at index kSmallTree is padding), so
-// the two paths share no registers (the kernel keeps its 243 VGPRs; 8
+// the two paths share no registers (the kernel stays within 256 VGPRs; 8
 // queries, 80 VGPRs of states beside two register tiles, spilled).  The
 // vector-ALU work grows with the queries while the matrix-core tile does
 // not, so the cut is at 2 nodes.  Measured on stress-shaped batches of 64
