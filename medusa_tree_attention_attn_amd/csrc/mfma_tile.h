@@ -48,6 +48,16 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// max(x, x of lane ^ 32) on the VALU: v_permlane32_swap exchanges the upper
+// lane half of one copy of x with the lower half of another, so that in every
+// lane the two results hold x of that lane and x of lane ^ 32 (in either
+// order).  One VALU instruction where a shuffle is an LDS permute round trip.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
@@ -148,7 +158,7 @@ __device__ __forceinline__ void compute_tile(WaveState& st, const u32x4 (&qf)[8]
   float tmax = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_xor32(tmax);
   const float m_new = (tmax > st.m + kSlack) ? tmax : st.m;
   const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);

@@ -74,24 +74,47 @@ struct Geo {
   int last_page;  // index of the split's last page in s_pages
 };
 
-// Issue the loads of context tile [tile0, tile0 + 64).  Pages past the
-// split's end load its last page again (store_tile zeroes their rows), so the
-// loads are unconditional and the compiler can count them.  Page ids are
+// The page ids of context tile [tile0, tile0 + 64): one 16-byte LDS read of
+// the four entries from base4 = min(pg0, last_page & ~3) on (pg0 is a
+// multiple of four; s_pages is 16-byte aligned and holds whole groups of
+// four).  The tile loop reads them before it computes the current tile, so
+// that only scalar address arithmetic stands between its barrier and the
+// next tile's loads.
+__device__ __forceinline__ u32x4 fetch_page_ids(const Geo& G, int tile0) {
+  const int pg0 = (tile0 - G.c0) >> 4;
+  const int base4 = min(pg0, G.last_page & ~3);
+  return *reinterpret_cast<const u32x4*>(G.s_pages + base4);
+}
+
+// Issue the loads of context tile [tile0, tile0 + 64) from its page ids.
+// Pages past the split's end load its last page again (store_tile zeroes
+// their rows), so the loads are unconditional and the compiler can count
+// them: page pg0 + p reads entry min(pg0 + p, last_page) - base4, which lies
+// in 0..3 whether or not the tile starts past the last page.  Page ids are
 // uniform, so page addresses are scalar; each lane adds a constant offset.
 // The KV stream is read once, so the loads carry the non-temporal hint: with
 // it the kernel streams at about 6.2 TB/s in steady state, against 5.6
 // without (7B-shaped batch 16: 63 against 70.5 us per launch).
-__device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int tile0, int tid) {
+__device__ __forceinline__ void issue_ctx_tile(TileRegs& R, const Geo& G, const u32x4 ids,
+                                               int tile0, int tid) {
   const int pg0 = (tile0 - G.c0) >> 4;
+  const int base4 = min(pg0, G.last_page & ~3);
   const int off = (tid >> 4) * kD + (tid & 15) * 8;
   const size_t v_plane = (size_t)G.Hkv * kPage * kD;
+  const int i0 = __builtin_amdgcn_readfirstlane(ids[0]), i1 = __builtin_amdgcn_readfirstlane(ids[1]);
+  const int i2 = __builtin_amdgcn_readfirstlane(ids[2]), i3 = __builtin_amdgcn_readfirstlane(ids[3]);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int blk = __builtin_amdgcn_readfirstlane(G.s_pages[min(pg0 + p, G.last_page)]);
+    const int e = min(pg0 + p, G.last_page) - base4;
+    const int blk = e == 0 ? i0 : e == 1 ? i1 : e == 2 ? i2 : i3;
     const uint16_t* kp = G.pages + page_row(blk, 0, G.hk, 0, G.Hkv, kD);
     R.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
     R.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + v_plane + off));
   }
+}
+
+__device__ __forceinline__ void load_ctx_tile(TileRegs& R, const Geo& G, int tile0, int tid) {
+  issue_ctx_tile(R, G, fetch_page_ids(G, tile0), tile0, tid);
 }
 
 // Rows at or past n_rows (the tokens of the context's last page after its
@@ -426,10 +449,12 @@ __device__ __forceinline__ void small_tree_item(const VerifyParams& p, const Geo
   int t = 1;
 #pragma unroll 1
   for (; t + 1 < n_tiles; t += 2) {
+    const u32x4 ia = fetch_page_ids(G, c0 + kTile * (t + 2));
+    const u32x4 ib = fetch_page_ids(G, c0 + kTile * (t + 3));
     consume(R, t);
-    load_ctx_tile(R, G, c0 + kTile * (t + 2), tid);
+    issue_ctx_tile(R, G, ia, c0 + kTile * (t + 2), tid);
     consume(R2, t + 1);
-    load_ctx_tile(R2, G, c0 + kTile * (t + 3), tid);
+    issue_ctx_tile(R2, G, ib, c0 + kTile * (t + 3), tid);
   }
   if (t < n_tiles) consume(R, t);
   if (sp == 0 && wv < 2) {  // the tree keys, rotated as stored (zero rows past t_real)
@@ -652,7 +677,7 @@ __device__ __forceinline__ bool launch_item(const VerifyParams& p, int slot, int
 __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(VerifyParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
   static_assert(4 * kHalfPark * sizeof(float) <= 2 * kStageBytes, "merge area");
-  __shared__ int s_pages[kMaxSplitPages];
+  __shared__ __attribute__((aligned(16))) int s_pages[kMaxSplitPages];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int qt = wv >> 1, th = wv & 1;
@@ -724,13 +749,15 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
   lds_sync();  // stage 0 filled; stage 1's tree or query reads done; tile 1 stays in flight
   if (n_tiles > 0) {
     // Every tile but the last is full: one straight-line path, no masking.
+    // The page ids of tile t + 2 are read from LDS before tile t is computed.
     for (int t = 0; t < n_tiles - 1; ++t) {
       char* cur = (t & 1) ? stage1 : stage0;
       char* nxt = (t & 1) ? stage0 : stage1;
+      const u32x4 ids = fetch_page_ids(G, c0 + kTile * (t + 2));
       if (active) compute_tile<kFull>(st, qf, cur, L, kTile, 0ull);
       store_tile(R, nxt, rows_of(t + 1), tid);
       __syncthreads();
-      if (t + 2 < n_tiles) load_ctx_tile(R, G, c0 + kTile * (t + 2), tid);
+      if (t + 2 < n_tiles) issue_ctx_tile(R, G, ids, c0 + kTile * (t + 2), tid);
     }
     // The last tile may end mid-tile.
     const int t = n_tiles - 1;
