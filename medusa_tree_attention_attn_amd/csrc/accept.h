@@ -1,12 +1,13 @@
 // Acceptance of one sequence's tree by one wavefront (LMDeploy PR #1231
 // evaluate_posterior), shared by the kernels that end in an acceptance.
 // Lane i = tree node i:
-//   ok_i     = edge parent(i) -> i passes its test (the root is always ok):
-//              greedy token match, or the typical-acceptance threshold
-//   M        = ballot(ok)
-//   anc_i    = ancestor-or-self set of i, by pointer doubling over the lanes
-//   accepted = every node on the root path is ok:  (anc_i & ~M) == 0
-//   end      = argmax over accepted nodes of (depth, -index)
+//   ok_i     = edge parent(i) -> i passes its test (the root is always ok)
+//   accepted = i is the root, or ok_i and parent(i) is accepted; found one
+//              tree level per step, each step one ballot over the lanes
+//              (a node is tested against the bitmask of the level above)
+//   end      = argmax over accepted nodes of (depth, -index): the lowest
+//              node of the deepest level found
+//   path     = end and its ancestors, read from the parent lanes
 #pragma once
 
 #include "common.h"
@@ -16,37 +17,44 @@ namespace ta {
 struct Acceptance {
   int len;          // accepted nodes, root included
   uint64_t path;    // bit k set iff node k is on the accepted path
-  int depth;        // this lane's depth in the tree (meaningful on linked lanes)
+  int depth;        // this lane's depth in the tree (meaningful on accepted lanes)
   bool in_tree;     // lane < T
 };
 
 // The accepted path of one tree, given each lane's (node's) parent and
 // whether its edge passed the test (`edge_ok`; the root's is ignored).
 // Called by one full wavefront; lane i = node i (lanes >= T: in_tree false,
-// parent kPadParent).
+// parent kPadParent).  A node is linked when it is the root with parent -1
+// or its parent precedes it; nodes that are not linked, or hang below one,
+// are never accepted, and a root that is not linked accepts nothing (len 0).
+// Everything but the parent's index stays in registers: the level loop
+// takes one ballot per tree level (at most 63) and the path walk one lane
+// read per level, where pointer doubling took six rounds of LDS permutes.
 __device__ __forceinline__ Acceptance select_path(int par, bool edge_ok, bool in_tree, int i) {
   const bool linked = (i == 0) ? (par == -1) : (par >= 0 && par < i);
   const bool ok = linked && (i == 0 || edge_ok);
-  const uint64_t M = __ballot(ok);
-
-  uint64_t anc = linked ? (1ull << i) : 0ull;
-  int up = (linked && i > 0) ? par : i;  // the root (and unlinked lanes) point at themselves
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {          // 2^6 - 1 >= 63 levels
-    const uint64_t a_up = __shfl(anc, up);
-    const int up_up = __shfl(up, up);
-    anc |= a_up;
-    up = up_up;
+  const int up = (linked && i > 0) ? par : 0;
+  uint64_t found = __ballot(i == 0 && ok);  // accepted so far: the root, if linked
+  uint64_t level = found;                   // the deepest level found
+  int depth = 0, d = 0;
+  while (level != 0ull) {  // uniform
+    const bool add = ok && i > 0 && ((level >> up) & 1ull) != 0ull;
+    const uint64_t next = __ballot(add);
+    if (next == 0ull) break;
+    ++d;
+    if (add) depth = d;
+    found |= next;
+    level = next;
   }
-  const bool rooted = (anc & 1ull) != 0ull;
-  const bool accepted = linked && rooted && ((anc & ~M) == 0ull);
-  const int depth = __popcll(anc) - 1;
-  int key = accepted ? (depth << 6) | (63 - i) : -1;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
-  const int end = 63 - (key & 63);       // key >= 0: the root is always accepted
-  const uint64_t anc_end = __shfl(anc, end);
-  return Acceptance{(int)__popcll(anc_end), anc_end, depth, in_tree};
+  uint64_t path = 0ull;
+  if (found != 0ull) {  // uniform
+    int n = __builtin_ctzll(level);
+    for (int k = d; k >= 0; --k) {
+      path |= 1ull << n;
+      n = __builtin_amdgcn_readlane(up, n);
+    }
+  }
+  return Acceptance{(int)__popcll(path), path, depth, in_tree};
 }
 
 // Greedy acceptance: edge parent(i) -> i passes iff cand_tokens[i] equals
