@@ -57,6 +57,13 @@ __device__ __forceinline__ float max_xor32(float x) {
       __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// x + x of lane ^ 32 the same way (the sum is commutative, so both lanes of
+// a pair get the same bits).
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }

@@ -296,17 +296,22 @@ __device__ __forceinline__ void store_out(const char* tile, const VerifyParams& 
 
 // Merge of the two token halves of a query tile, shared by its two
 // wavefronts: wavefront th keeps d-tiles 2th and 2th+1 of O^T.  Each parks
-// the other pair and its (m, l) in a lane-major block of 34 x 64 floats, and
-// after a barrier merges its own pair with the pair its partner parked.  The
-// running sums are combined in one fixed order (th = 0's first), so both
-// wavefronts hold the same l.
+// the other pair and its (m, l) in a block of 34 x 64 floats (eight
+// lane-major groups of four accumulators, written and read 16 bytes per
+// lane, then m and l), and after a barrier merges its own pair with the pair
+// its partner parked.  The running sums are combined in one fixed order
+// (th = 0's first), so both wavefronts hold the same l.
 constexpr int kHalfPark = 34 * 64;  // floats per wavefront
 template <int kDOther>
 __device__ __forceinline__ void park_half(const WaveState& st, float* blk, int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) blk[(16 * j + r) * 64 + lane] = st.o[kDOther + j][r];
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x16& o = st.o[kDOther + j];
+      *reinterpret_cast<f32x4*>(blk + ((4 * j + r4) * 64 + lane) * 4) =
+          f32x4{o[4 * r4], o[4 * r4 + 1], o[4 * r4 + 2], o[4 * r4 + 3]};
+    }
   blk[32 * 64 + lane] = st.m;
   blk[33 * 64 + lane] = st.l;
 }
@@ -321,8 +326,12 @@ __device__ __forceinline__ void merge_half(WaveState& st, const float* pblk, int
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      st.o[d_own + j][r] = st.o[d_own + j][r] * w_own + pblk[(16 * j + r) * 64 + lane] * w_par;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(pblk + ((4 * j + r4) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        st.o[d_own + j][4 * r4 + e] = st.o[d_own + j][4 * r4 + e] * w_own + x[e] * w_par;
+    }
   const float la = kTh == 0 ? st.l : l1, wa = kTh == 0 ? w_own : w_par;
   const float lb = kTh == 0 ? l1 : st.l, wb = kTh == 0 ? w_par : w_own;
   st.l = la * wa + lb * wb;
@@ -796,7 +805,7 @@ __global__ __launch_bounds__(kThreads, TA_WG_PER_CU) void verify_mfma_kernel(Ver
       merge_half<0>(st, park + (2 * qt + 1) * kHalfPark, lane);
     else
       merge_half<1>(st, park + (2 * qt) * kHalfPark, lane);
-    st.l += __shfl_xor(st.l, 32);
+    st.l = sum_xor32(st.l);
   }
   if (nsplit == 1) {  // uniform
     char* tile = last_stage;

@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kSThreads, 1) void verify_stream_kernel(VerifyParam
         const int s2 = 2 * qt + 1;
         if (active) {
           merge_state(st, park + s2 * kParkO, s_ml[s2][0][lane], s_ml[s2][1][lane], lane);
-          st.l += __shfl_xor(st.l, 32);
+          st.l = sum_xor32(st.l);
         }
         write_result(st, p, U.b, U.h, U.b * p.H + U.h, U.sp, U.nsplit, q, T, row_real, lane >> 5);
       }
