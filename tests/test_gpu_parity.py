@@ -350,6 +350,43 @@ def test_accept_all_and_none_match():
         assert np.array_equal(L, Lr) and np.array_equal(P, Pr)
 
 
+
+@pytest.mark.parametrize("mismatch_depth", [None, 1, 17, 40, 63])
+def test_accept_deep_chains(mismatch_depth):
+    """Chains of 64 nodes (depth 63), where the acceptance takes one step per
+    tree level and reads the path back through every level: every edge
+    matches, or the first mismatch sits at a given depth (at another depth
+    in the second sequence; the third matches throughout).  The separate
+    acceptance and the fused acceptance + commit against the oracle, the
+    whole pool bit for bit."""
+    import dataclasses
+    wl = make_workload("vicuna7b_bs1", 5, batch=3, heads=2, ctx_range=(1, 200),
+                       tree_sizes=(64,), chain=True)
+    dep = np.asarray(wl.tree_depth)
+    assert dep.max() == 63
+    amax = np.full_like(wl.node_argmax, 7)
+    cand = np.full_like(wl.cand_tokens, 7)
+    if mismatch_depth is not None:
+        cand[0][dep[0] == mismatch_depth] = 8
+        cand[1][dep[1] == (mismatch_depth + 1) // 2] = 8
+    wl = dataclasses.replace(wl, node_argmax=amax, cand_tokens=cand)
+    Lr, Pr = oracle.accept_greedy(amax, cand, wl.tree_parent)
+    expect = [mismatch_depth or 64, (mismatch_depth + 1) // 2 if mismatch_depth else 64, 64]
+    assert list(Lr) == expect
+    L, P = _accept_gpu(wl)
+    assert np.array_equal(L, Lr) and np.array_equal(P, Pr)
+    d = dev(wl)
+    tv = verifier(wl)
+    L2, P2 = tv.accept_commit(d["node_argmax"], d["cand_tokens"], d["tree_parent"], d["k_new"],
+                              d["v_new"], d["kv_pages"], d["block_table"], d["ctx_lens"])
+    torch.cuda.synchronize()
+    assert np.array_equal(L2.cpu().numpy(), Lr) and np.array_equal(P2.cpu().numpy(), Pr)
+    rope = oracle.rope_table(wl.spec.head_dim, wl.max_ctx_len + wl.spec.t_max)
+    ref = oracle.commit(wl.k_new, wl.v_new, Lr, Pr, wl.kv_pages, wl.block_table, wl.ctx_lens,
+                        rope)
+    assert torch.equal(pool_bits(d["kv_pages"].cpu()), pool_bits(ref))
+
+
 # ----------------------------------------------------------------- commit --
 
 def _commit_gpu(wl, L=None, P=None):
