@@ -74,6 +74,10 @@ SPECS: Dict[str, WorkloadSpec] = {
     # has only its root (T = 1)
     "decode_b64": WorkloadSpec("decode_b64", 64, 32, 32, 128, "bf16",
                                (128, 8192), (1,), 0, 32000, 0.25, t_max=1),
+    # the 7B batch-16 shape with grouped query heads: 32 query heads sharing
+    # 8 KV heads (4 per KV head)
+    "gqa_b16": WorkloadSpec("gqa_b16", 16, 32, 8, 128, "bf16",
+                            (256, 2048), (64,), 4, 32000, 0.3),
 }
 
 
@@ -223,6 +227,7 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
                   tree_sizes: Optional[tuple] = None,
                   max_depth: Optional[int] = None,
                   heads: Optional[int] = None,
+                  kv_heads: Optional[int] = None,
                   head_dim: Optional[int] = None,
                   chain: bool = False,
                   extra_pool_blocks: int = 0) -> Workload:
@@ -244,6 +249,8 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
     if heads is not None:
         repl["heads"] = heads
         repl["kv_heads"] = heads
+    if kv_heads is not None:
+        repl["kv_heads"] = kv_heads
     if head_dim is not None:
         repl["head_dim"] = head_dim
     if repl:

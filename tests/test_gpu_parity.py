@@ -206,6 +206,27 @@ def test_verify_grouped_query_heads(kernel):
     _check_rows(got, ref, wl, [0, 1])
 
 
+
+@pytest.mark.parametrize("batch,kv_heads,split_tokens,ctx_range", [
+    (3, 8, 0, (100, 700)),     # fewer items than CUs
+    (9, 8, 0, (100, 700)),     # 288 items: long and short halves on shared CUs
+    (9, 4, 256, (100, 700)),   # split items (ranked groups of (sequence, split))
+    (3, 2, 0, (100, 700)),     # 16 query heads per KV head
+    (66, 8, 0, (1, 90)),       # more than 64 groups: (sequence, head) order
+], ids=["b3-kv8", "b9-kv8", "b9-kv4-split", "b3-kv2", "b66-kv8"])
+def test_verify_grouped_heads_launch_order(batch, kv_heads, split_tokens, ctx_range):
+    """32 query heads on fewer KV heads: the launch order puts the query heads
+    of one KV head on one XCD (a permutation of the heads of each (sequence,
+    split) group).  Every head of every sequence (of the first nine at batch
+    66) against the oracle."""
+    wl = make_workload("vicuna7b_b16", 12, batch=batch, heads=32, kv_heads=kv_heads,
+                       ctx_range=ctx_range)
+    got = _verify_gpu(wl, split_tokens=split_tokens)
+    seqs = list(range(min(batch, 9)))
+    ref = oracle_verify_rows(wl, seqs)
+    _check_rows(got[seqs], ref, wl, seqs)
+
+
 MIXED_SIZES = (1, 2, 4, 8, 26, 64)
 
 
