@@ -269,7 +269,10 @@ def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
     for b in range(B):
         n = int(sizes[b])
         if spec.full_binary and not chain:
-            pb = full_binary_tree(spec.max_depth)[:n]
+            d = spec.max_depth  # deep enough for n nodes (a size override may ask for more)
+            while 2 ** (d + 1) - 1 < n:
+                d += 1
+            pb = full_binary_tree(d)[:n]
         elif chain:
             pb = np.arange(-1, n - 1, dtype=np.int32)
         else:

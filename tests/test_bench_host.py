@@ -100,3 +100,17 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_full_binary_preset_takes_larger_tree_sizes():
+    """The preset built on a fixed full binary tree grows the tree to a
+    requested size: every sequence's real nodes are a prefix of a full binary
+    tree in BFS order (node i's parent is (i - 1) // 2), as many as drawn."""
+    wl = make_workload("tiny", 4, batch=6, heads=1, tree_sizes=(1, 5, 26, 63))
+    assert wl.spec.t_max == 63
+    for b in range(6):
+        par = np.asarray(wl.tree_parent[b])
+        n = int(np.sum(par != -2))
+        assert n in (1, 5, 26, 63)
+        assert par[0] == -1 and all(par[i] == (i - 1) // 2 for i in range(1, n))
+        assert np.all(par[n:] == -2)
