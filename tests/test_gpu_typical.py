@@ -129,3 +129,27 @@ def test_typical_accept_one_node_trees():
     assert L.cpu().tolist() == [1] * 5
     assert P.cpu()[:, 0].tolist() == [0] * 5
     assert OK.cpu()[:, 0].tolist() == [1] * 5
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_typical_accept_random_shapes(case):
+    """Seeded random combinations of batch, tree sizes, vocabulary, dtype,
+    temperature, thresholds, logit scale and masked tails."""
+    import random
+    rng = random.Random(4000 + case)
+    vocab = rng.choice([12, 64, 1001, 4096, 32000, 50257])
+    mask = rng.choice([0, 0, vocab // 4])
+    kw = dict(batch=rng.randint(1, 8),
+              tree_sizes=tuple(sorted(rng.sample([1, 2, 3, 5, 8, 16, 26, 40, 63, 64],
+                                                 rng.randint(1, 3)))))
+    dtype = rng.choice([torch.bfloat16, torch.float32])
+    scale = rng.choice([0.5, 1.0, 2.0, 3.0])
+    margin = rng.choice([0.0, 1.0, 4.0])
+    temp = rng.choice([0.5, 0.7, 1.0, 1.5, 2.0])
+    eps, delta = rng.choice([(0.09, 0.3), (0.5, 0.5), (1e-3, 0.1), (0.2, 0.9)])
+    seed = rng.randint(0, 10**6)
+    print(f"random typical {case}: seed {seed} {kw} V {vocab} masked {mask} {dtype} "
+          f"scale {scale} margin {margin} T {temp} eps {eps} delta {delta}", flush=True)
+    wl, logits, cand = _inputs("vicuna7b_b16", seed, kw, vocab, dtype, scale, margin,
+                               mask_tail=mask)
+    _check(wl, logits, cand, temp, eps, delta)
